@@ -1,0 +1,242 @@
+"""Exact per-row top-k selection for AMD MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/ets_topk.h`` (library
+``libets_topk.so``, built from ``csrc/ets_topk.hip``).  This module only
+checks and marshals arguments: every step of the selection runs in the HIP
+kernels.  PyTorch provides device memory and the current stream.
+
+Entry points (same names as the C ABI without the ``ets_`` prefix):
+
+* :func:`topk_raw`    -- dense rows, row-local positions;
+* :func:`topk_paged`  -- dense rows, paged KV slots through a page table
+  (argument order of the pages' fused transform: scores, seq_lens,
+  page_table, output, page_size);
+* :func:`topk_ragged` -- packed ragged rows, packed-buffer positions.
+
+Each output row holds min(k, n) selected entries in unspecified order followed
+by -1 padding.  Scores are ranked by their order-preserving 32-bit key; among
+equal bit patterns the lowest positions win.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+__all__ = ["topk_raw", "topk_paged", "topk_ragged", "workspace_size", "row_split",
+           "library_path", "MAX_K", "EtsError"]
+
+MAX_K = 2048
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libets_topk.so")
+_lock = threading.Lock()
+_lib = None
+
+
+class EtsError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, _status_text(status), status))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(
+                    "libets_topk.so is not built (expected at %s); run "
+                    "`python -c 'import __graft_entry__ as g; g.build()'` first" % _LIB_PATH)
+            lib = ctypes.CDLL(_LIB_PATH)
+            vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+            lib.ets_topk_raw.argtypes = [vp, i64, i32, i32, vp, i32, vp, i64, vp, sz, vp]
+            lib.ets_topk_paged.argtypes = [vp, i64, i32, i32, vp, vp, i64, i32, i32, vp, i64,
+                                           vp, sz, vp]
+            lib.ets_topk_ragged.argtypes = [vp, vp, vp, i32, i64, i32, vp, i64, vp, sz, vp]
+            lib.ets_workspace_size.argtypes = [i32, i64, i32, i32, ctypes.POINTER(sz)]
+            lib.ets_row_split.argtypes = [i32, i64, i32]
+            lib.ets_status_string.argtypes = [i32]
+            for fn in (lib.ets_topk_raw, lib.ets_topk_paged, lib.ets_topk_ragged,
+                       lib.ets_workspace_size, lib.ets_row_split):
+                fn.restype = ctypes.c_int32
+            lib.ets_status_string.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return _load().ets_status_string(status).decode()
+    except Exception:  # pragma: no cover - library unavailable
+        return "status %d" % status
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise EtsError(status, what)
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype, dim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != dim:
+        raise ValueError("%s must be %d-D, got shape %s" % (name, dim, tuple(t.shape)))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a HIP device, got %s" % (name, t.device))
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Row stride (elements) of a 2-D tensor whose rows are contiguous."""
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s rows must be contiguous (stride(1) == 1)" % name)
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def _vec(t: torch.Tensor, name: str, n: int) -> None:
+    _require(t, name, torch.int32, 1)
+    if t.shape[0] != n:
+        raise ValueError("%s must have %d entries, got %d" % (name, n, t.shape[0]))
+    if n > 1 and t.stride(0) != 1:
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_size(B: int, max_row_len: int, k: int, device: Optional[int] = None) -> int:
+    """Bytes of workspace a call with these sizes needs (0 if none)."""
+    nbytes = ctypes.c_size_t(0)
+    _check(_load().ets_workspace_size(B, max_row_len, k, -1 if device is None else device,
+                                      ctypes.byref(nbytes)), "ets_workspace_size")
+    return nbytes.value
+
+
+def row_split(B: int, max_row_len: int, cu_count: int) -> int:
+    """Blocks per row chosen for (B, max_row_len) on ``cu_count`` CUs (0 = one per row)."""
+    return int(_load().ets_row_split(B, max_row_len, cu_count))
+
+
+def _workspace(B: int, max_len: int, k: int, device: torch.device,
+               workspace: Optional[torch.Tensor]):
+    with torch.cuda.device(device):
+        need = workspace_size(B, max_len, k)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.device != device or workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace must be on %s with at least %d bytes" % (device, need))
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _out(out: Optional[torch.Tensor], B: int, k: int, device: torch.device) -> torch.Tensor:
+    if out is None:
+        return torch.empty((B, k), dtype=torch.int32, device=device)
+    _require(out, "out", torch.int32, 2)
+    if out.shape[0] != B or out.shape[1] < k or out.device != device:
+        raise ValueError("out must be int32 [B, >=k] on %s" % device)
+    if k > 1 and out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous")
+    return out
+
+
+def topk_raw(scores: torch.Tensor, k: int, lens: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Exact top-k positions of each row of fp32 ``scores`` [B, L]; int32 [B, k]."""
+    _require(scores, "scores", torch.float32, 2)
+    B, L = scores.shape
+    dev = scores.device
+    if lens is not None:
+        _vec(lens, "lens", B)
+        if lens.device != dev:
+            raise ValueError("lens must be on %s" % dev)
+    out = _out(out, B, k, dev)
+    ws, ws_bytes = _workspace(B, L, k, dev, workspace)
+    with torch.cuda.device(dev):
+        st = _load().ets_topk_raw(scores.data_ptr(), _rows(scores, "scores"), B, L,
+                                  lens.data_ptr() if lens is not None else None, k,
+                                  out.data_ptr(), out.stride(0) if B > 1 else k,
+                                  ws.data_ptr() if ws is not None else None, ws_bytes,
+                                  _stream(dev))
+    _check(st, "ets_topk_raw")
+    return out
+
+
+def topk_paged(scores: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.Tensor,
+               page_indices: torch.Tensor, page_size: int,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fills ``page_indices`` int32 [B, k] with the paged slots of each row's top-k.
+
+    Slot of position i of row b: page_table[b, i // page_size] * page_size +
+    i % page_size.  ``k`` is ``page_indices.shape[1]``.
+    """
+    _require(scores, "scores", torch.float32, 2)
+    B, L = scores.shape
+    dev = scores.device
+    _vec(seq_lens, "seq_lens", B)
+    _require(page_table, "page_table", torch.int32, 2)
+    if page_table.shape[0] != B:
+        raise ValueError("page_table must have B rows")
+    _require(page_indices, "page_indices", torch.int32, 2)
+    k = page_indices.shape[1]
+    out = _out(page_indices, B, k, dev)
+    for t, nm in ((seq_lens, "seq_lens"), (page_table, "page_table")):
+        if t.device != dev:
+            raise ValueError("%s must be on %s" % (nm, dev))
+    if page_size < 1:
+        raise ValueError("page_size must be >= 1")
+    if page_table.shape[1] * page_size < L:
+        raise ValueError("page_table has %d pages of %d, fewer than L = %d positions"
+                         % (page_table.shape[1], page_size, L))
+    ws, ws_bytes = _workspace(B, L, k, dev, workspace)
+    with torch.cuda.device(dev):
+        st = _load().ets_topk_paged(scores.data_ptr(), _rows(scores, "scores"), B, L,
+                                    seq_lens.data_ptr(), page_table.data_ptr(),
+                                    _rows(page_table, "page_table"), page_size, k,
+                                    out.data_ptr(), out.stride(0) if B > 1 else k,
+                                    ws.data_ptr() if ws is not None else None, ws_bytes,
+                                    _stream(dev))
+    _check(st, "ets_topk_paged")
+    return out
+
+
+def topk_ragged(packed: torch.Tensor, row_starts: torch.Tensor, lengths: torch.Tensor, k: int,
+                max_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Exact top-k of packed ragged rows; int32 [B, k] of packed-buffer positions.
+
+    ``max_len`` bounds every length; if omitted it is read from ``lengths``,
+    which synchronises the stream.
+    """
+    _require(packed, "packed", torch.float32, 1)
+    dev = packed.device
+    B = row_starts.shape[0]
+    _vec(row_starts, "row_starts", B)
+    _vec(lengths, "lengths", B)
+    if packed.numel() > 1 and packed.stride(0) != 1:
+        raise ValueError("packed must be contiguous")
+    if max_len is None:
+        max_len = int(lengths.max().item()) if B else 0
+    out = _out(out, B, k, dev)
+    ws, ws_bytes = _workspace(B, max_len, k, dev, workspace)
+    with torch.cuda.device(dev):
+        st = _load().ets_topk_ragged(packed.data_ptr(), row_starts.data_ptr(),
+                                     lengths.data_ptr(), B, max_len, k, out.data_ptr(),
+                                     out.stride(0) if B > 1 else k,
+                                     ws.data_ptr() if ws is not None else None, ws_bytes,
+                                     _stream(dev))
+    _check(st, "ets_topk_ragged")
+    return out

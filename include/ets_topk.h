@@ -1,0 +1,139 @@
+/*
+ * ets_topk.h -- C ABI of the exact per-row top-k selection library for
+ * AMD MI355X (gfx950).
+ *
+ * What is computed (sglang PR #37591 digest, "Summary" and "Implementation
+ * breakdown" item 1): for every row b of fp32 scores, the positions of the k
+ * largest scores of the row's valid part, exactly.  Scores are ranked by the
+ * order-preserving 32-bit key of their bit pattern (same page, the
+ * order_key32 excerpt: negative values have every bit inverted, non-negative
+ * values get the sign bit set, and unsigned comparison of keys then equals
+ * float comparison).  Consequences of ranking by key:
+ *   - +0.0 ranks above -0.0, subnormals are ordered by their bits (no flush
+ *     to zero), +NaN ranks above +inf and -NaN below -inf;
+ *   - "equal scores" means identical bit patterns; among equal scores the
+ *     lowest positions are taken, so the selected set is unique.
+ *
+ * Output (sglang PR #36004 digest, test excerpt; PR #37591 digest, the
+ * CoopParams / OutMap excerpt): each row of `out` receives m = min(k, n)
+ * mapped positions followed by k - m entries of -1.  The m entries appear in
+ * an unspecified (but run-to-run deterministic) order; compare them as sets.
+ * Every one of the k slots is written; prior contents of `out` do not matter.
+ * Position maps:
+ *   raw    : i                                          (row-local position)
+ *   paged  : page_table[b][i / page_size] * page_size + i % page_size
+ *   ragged : row_starts[b] + i                          (packed-buffer position)
+ *
+ * Conventions shared by every call:
+ *   - All array pointers are device memory owned by the caller.  The library
+ *     allocates nothing on the device and never synchronises the host; work
+ *     is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *   - Arguments are validated on the host before any HIP call; a rejected
+ *     call enqueues nothing.  Device-side preconditions are not checked:
+ *     page ids must be >= 0 with page_id * page_size + page_size - 1 < 2^31,
+ *     and ragged rows must lie inside the packed buffer.
+ *   - Only gfx950 devices are supported; others return ETS_ERR_DEVICE.
+ *   - `workspace` is caller-owned device memory of at least the size that
+ *     ets_workspace_size() reports for the same (B, max row length, k) on the
+ *     current device (0 bytes is valid; then workspace may be NULL).  It must
+ *     not be shared by calls that may run concurrently.  Its contents between
+ *     calls are irrelevant: every call initialises what it uses on `stream`.
+ */
+#ifndef ETS_TOPK_H
+#define ETS_TOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ets_status;
+
+#define ETS_OK 0
+#define ETS_ERR_INVALID_ARG 1 /* null pointer, negative size, bad stride or page size */
+#define ETS_ERR_K_RANGE 2     /* k outside [1, ETS_MAX_K] */
+#define ETS_ERR_WORKSPACE 3   /* workspace smaller than ets_workspace_size() */
+#define ETS_ERR_DEVICE 4      /* current device is not gfx950 or cannot be queried */
+#define ETS_ERR_HIP 5         /* a HIP launch or runtime call failed */
+
+/* Largest supported k (the pages fix k at 1024 for the paged transform,
+ * PR #36004 digest, kMaxTopK excerpt, and at 2048 for the DSA top-k,
+ * PR #37591 digest, "Implementation breakdown" item 2). */
+#define ETS_MAX_K 2048
+
+/*
+ * Dense rows, raw output.
+ *   scores     fp32 [B, row_stride] (row b starts at scores + b * row_stride);
+ *              only the first L entries of a row are ever read.
+ *   row_stride elements between consecutive rows, >= L.
+ *   B, L       batch size (>= 0) and row capacity (>= 0).
+ *   lens       int32 [B] valid length of each row, clamped to [0, L];
+ *              NULL means every row is L long.
+ *   k          1 <= k <= ETS_MAX_K.
+ *   out        int32 [B, out_stride], out_stride >= k; row-local positions.
+ */
+ets_status ets_topk_raw(const float* scores, int64_t row_stride, int32_t B, int32_t L,
+                        const int32_t* lens, int32_t k, int32_t* out, int64_t out_stride,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dense rows, paged output (PR #36004 digest: the fused top-k + page-table
+ * transform, called with scores, seq_lens, page_table, the output and
+ * page_size).
+ *   seq_lens   int32 [B] valid length of each row (clamped to [0, L]); required.
+ *   page_table int32 [B, pt_stride]; row b needs ceil(min(seq_lens[b], L) /
+ *              page_size) entries.
+ *   page_size  >= 1.
+ *   out        int32 [B, out_stride]: page_table[b][i / page_size] *
+ *              page_size + i % page_size for each selected position i.
+ */
+ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, int32_t L,
+                          const int32_t* seq_lens, const int32_t* page_table, int64_t pt_stride,
+                          int32_t page_size, int32_t k, int32_t* out, int64_t out_stride,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Packed ragged rows (PR #37591 digest, CoopParams excerpt: row_starts and
+ * lengths address the rows of one packed buffer).
+ *   packed       fp32 buffer holding every row.
+ *   row_starts   int32 [B] offset of row b in `packed` (>= 0).
+ *   lengths      int32 [B] length of row b (negative counts as 0).
+ *   max_len_hint an upper bound of every lengths[b] (the host cannot read
+ *                device lengths without a sync); it only steers the launch
+ *                shape and the workspace size.  A row longer than the hint
+ *                is still handled exactly when workspace is large enough for
+ *                the longer length.
+ *   out          int32 [B, out_stride]: row_starts[b] + i per selected i.
+ */
+ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,
+                           const int32_t* lengths, int32_t B, int64_t max_len_hint, int32_t k,
+                           int32_t* out, int64_t out_stride, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes needed by a call with this batch size, longest row and k on
+ * `device` (-1 = the current device).  Writes 0 when the call needs none.
+ */
+ets_status ets_workspace_size(int32_t B, int64_t max_row_len, int32_t k, int32_t device,
+                              size_t* bytes);
+
+/*
+ * Blocks per row the library uses for (B, max_row_len) on a device with
+ * `cu_count` compute units; 0 means one block per row.  Pure host function.
+ * The environment variable ETS_ROW_SPLIT, when set to an integer >= 0,
+ * overrides the heuristic (0 forces one block per row).  After the pages'
+ * row_split heuristic (PR #37591 digest, the topk.hip excerpt), with
+ * constants of this library.
+ */
+int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count);
+
+/* Static, human-readable text for a status code. */
+const char* ets_status_string(ets_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ETS_TOPK_H */

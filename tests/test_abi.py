@@ -1,0 +1,97 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ets_topk.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:ets_status|int32_t|const char\*)\s+(ets_\w+)\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import exact_top_selection_amd as ets
+    if not os.path.exists(ets.library_path()):
+        from exact_top_selection_amd import _build
+        _build.build()
+    return ets._load()
+
+
+def test_header_declares_the_api():
+    assert {"ets_topk_raw", "ets_topk_paged", "ets_topk_ragged", "ets_workspace_size",
+            "ets_row_split", "ets_status_string"} <= set(_declared())
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ets_\w+)$", out, re.M))
+    assert set(_declared()) <= exported
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "ets_topk.h"\nint main(void){ return ETS_OK; }\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                    str(src), "-o", str(tmp_path / "use")], check=True)
+
+
+def test_status_strings(lib):
+    for s in range(0, 6):
+        assert lib.ets_status_string(s)
+    assert b"unknown" in lib.ets_status_string(99)
+
+
+def test_host_validation_rejects_before_device_work(lib):
+    vp = ctypes.c_void_p
+    fake = vp(0x1000)  # never dereferenced: validation fails first
+    # k out of range
+    assert lib.ets_topk_raw(fake, 64, 1, 64, None, 0, fake, 64, None, 0, None) == 2
+    assert lib.ets_topk_raw(fake, 64, 1, 64, None, 2049, fake, 4096, None, 0, None) == 2
+    # negative sizes, bad strides
+    assert lib.ets_topk_raw(fake, 64, -1, 64, None, 8, fake, 8, None, 0, None) == 1
+    assert lib.ets_topk_raw(fake, 32, 1, 64, None, 8, fake, 8, None, 0, None) == 1
+    assert lib.ets_topk_raw(fake, 64, 1, 64, None, 8, fake, 4, None, 0, None) == 1
+    # null output / scores
+    assert lib.ets_topk_raw(fake, 64, 1, 64, None, 8, None, 8, None, 0, None) == 1
+    assert lib.ets_topk_raw(None, 64, 1, 64, None, 8, fake, 8, None, 0, None) == 1
+    # paged: bad page size, missing seq_lens / page table
+    assert lib.ets_topk_paged(fake, 64, 1, 64, fake, fake, 1, 0, 8, fake, 8, None, 0, None) == 1
+    assert lib.ets_topk_paged(fake, 64, 1, 64, None, fake, 1, 64, 8, fake, 8, None, 0, None) == 1
+    assert lib.ets_topk_paged(fake, 64, 1, 64, fake, None, 1, 64, 8, fake, 8, None, 0, None) == 1
+    # ragged: missing arrays, negative hint
+    assert lib.ets_topk_ragged(fake, None, fake, 1, 10, 8, fake, 8, None, 0, None) == 1
+    assert lib.ets_topk_ragged(fake, fake, fake, 1, -1, 8, fake, 8, None, 0, None) == 1
+    # an empty batch is a no-op that needs no device
+    assert lib.ets_topk_raw(None, 0, 0, 0, None, 8, None, 8, None, 0, None) == 0
+
+
+def test_workspace_query_validation(lib):
+    n = ctypes.c_size_t(123)
+    assert lib.ets_workspace_size(4, 1000, 0, -1, ctypes.byref(n)) == 2
+    assert lib.ets_workspace_size(-1, 1000, 8, -1, ctypes.byref(n)) == 1
+    assert lib.ets_workspace_size(4, 1000, 8, -1, None) == 1
+
+
+def test_row_split_env_override(tmp_path):
+    code = ("import exact_top_selection_amd as e; "
+            "print(e.row_split(4, 262144, 256), e.row_split(64, 32768, 256))")
+    env = dict(os.environ, ETS_ROW_SPLIT="7", PYTHONPATH=ROOT)
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                         check=True).stdout.split()
+    assert out == ["7", "7"]
+    env["ETS_ROW_SPLIT"] = "0"
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                         check=True).stdout.split()
+    assert out == ["0", "0"]

@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element.
+
+Bar: bit-exact sorted index sets per row (including the count of -1 padding)
+and equal value multisets by bit pattern.  Inputs are seeded and synthetic.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import exact_top_selection_amd as ets
+import workloads
+from workloads import Workload
+from tests.gpu_helpers import POISON, assert_parity, dev, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_rows.json")
+
+
+def _dense(name, api, scores, k, lens=None, ps=64, pt=None):
+    B, L = scores.shape
+    if api == "paged":
+        if lens is None:
+            lens = np.full(B, L, dtype=np.int32)
+        if pt is None:
+            npg = (L + ps - 1) // ps
+            pt = np.broadcast_to(np.arange(npg, dtype=np.int32), (B, npg)).copy()
+        return Workload(name, "paged", k, B, scores, L=L, lens=lens.astype(np.int32),
+                        page_table=pt.astype(np.int32), page_size=ps)
+    return Workload(name, "raw", k, B, scores, L=L,
+                    lens=None if lens is None else lens.astype(np.int32))
+
+
+@pytest.mark.parametrize("seed", [42, 43])
+@pytest.mark.parametrize("name", workloads.NAMES)
+def test_named_workloads(name, seed):
+    w = workloads.make(name, seed=seed)
+    print("case", name, "seed", seed, flush=True)
+    got = run_gpu(w)
+    assert_parity(w, got, run_oracle(w))
+
+
+def test_named_workloads_deterministic():
+    for name in ("C3", "C4"):
+        w = workloads.make(name, seed=44)
+        a = run_gpu(w)
+        b = run_gpu(w, out_fill=-5)
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("k", [1, 7, 1024, 2048])
+def test_short_and_boundary_lengths(k):
+    rng = np.random.default_rng(k)
+    L = 2 * k + 64
+    lens = np.array([0, 1, 2, 3, 5, max(k - 1, 0), k, k + 1, 2 * k, L], dtype=np.int32)
+    x = rng.standard_normal((lens.shape[0], L)).astype(np.float32)
+    w = _dense("short", "raw", x, k, lens)
+    assert_parity(w, run_gpu(w), run_oracle(w))
+    # an infinite tail beyond each row's length must be ignored
+    poisoned = x.copy()
+    for b, n in enumerate(lens):
+        poisoned[b, n:] = np.inf
+    got = run_gpu(w, scores=poisoned)
+    assert_parity(w, got, run_oracle(w), check_values=False)
+
+
+def test_golden_hand_rows():
+    cases = json.load(open(GOLDEN))["cases"]
+    for case in cases:
+        bits = np.array([int(b, 16) for b in case["bits"]], dtype=np.uint32)
+        n = bits.shape[0]
+        L = max(n, 4)
+        row = np.zeros((1, L), dtype=np.uint32)
+        row[0, :n] = bits
+        w = _dense(case["name"], "raw", row.view(np.float32), case["k"],
+                   np.array([n], dtype=np.int32))
+        got = run_gpu(w)[0]
+        assert sorted(got[got != -1].tolist()) == case["expect"], case["name"]
+        assert int((got == -1).sum()) == case["k"] - len(case["expect"]), case["name"]
+
+
+@pytest.mark.parametrize("k", [1, 1024, 2048])
+@pytest.mark.parametrize("L", [2048, 32768])
+def test_all_equal_rows(k, L):
+    x = np.full((3, L), 0.75, dtype=np.float32)
+    x[1] = -0.0
+    x[2] = np.float32(1.0e-40)  # subnormal
+    w = _dense("equal", "raw", x, k)
+    assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+def test_all_subnormal_and_signed_zero_rows():
+    rng = np.random.default_rng(5)
+    L = 20000
+    sub = rng.integers(1, 1 << 23, size=(2, L), dtype=np.uint32)
+    sub[1] |= np.uint32(0x80000000)
+    zeros = np.where(rng.random((1, L)) < 0.5, np.uint32(0), np.uint32(0x80000000)).astype(np.uint32)
+    x = np.concatenate([sub, zeros]).view(np.float32)
+    for k in (1024, 2048):
+        w = _dense("subnormal", "raw", x, k)
+        assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+@pytest.mark.parametrize("pool", [1, 2, 3, 17, 300])
+def test_heavy_ties(pool):
+    rng = np.random.default_rng(pool)
+    vals = rng.standard_normal(pool).astype(np.float32)
+    x = vals[rng.integers(0, pool, size=(6, 32768))]
+    lens = np.array([32768, 30000, 4097, 2049, 1025, 20000], dtype=np.int32)
+    for k in (1024, 2048):
+        w = _dense("ties", "raw", x, k, lens)
+        assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+def test_concentrated_rows_small_batch():
+    rng = np.random.Generator(np.random.PCG64(9))
+    x = np.stack([workloads.concentrated_row(rng, 32768) for _ in range(6)])
+    lens = np.array([32768, 32768, 20000, 5000, 3000, 2049], dtype=np.int32)
+    for k in (1024, 2048):
+        w = _dense("concentrated", "raw", x, k, lens)
+        assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+@pytest.mark.parametrize("L", [32769, 70001, 100000])
+def test_rows_longer_than_one_tile(L):
+    rng = np.random.default_rng(L)
+    x = rng.standard_normal((3, L)).astype(np.float32)
+    lens = np.array([L, L - 1, 40000], dtype=np.int32)
+    for k in (1024, 2048):
+        w = _dense("long", "raw", x, k, lens)
+        assert_parity(w, run_gpu(w), run_oracle(w))
+    rng2 = np.random.Generator(np.random.PCG64(L))
+    y = np.stack([workloads.concentrated_row(rng2, L) for _ in range(2)])
+    w = _dense("long-concentrated", "raw", y, 2048)
+    assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+@pytest.mark.parametrize("L", [8191, 4099])
+def test_unaligned_rows(L):
+    """Odd row capacity: the scalar-load layout."""
+    rng = np.random.default_rng(L)
+    x = rng.standard_normal((4, L)).astype(np.float32)
+    lens = np.array([L, L - 3, 1500, 1024], dtype=np.int32)
+    w = _dense("unaligned", "raw", x, 1024, lens)
+    assert_parity(w, run_gpu(w), run_oracle(w))
+    # a row-stride view that is not a multiple of four
+    big = rng.standard_normal((4, L + 1)).astype(np.float32)
+    t = torch.from_numpy(big).to(dev())[:, :L]
+    out = ets.topk_raw(t, 1024, torch.from_numpy(lens).to(dev()))
+    w2 = _dense("strided", "raw", np.ascontiguousarray(big[:, :L]), 1024, lens)
+    assert_parity(w2, out.cpu().numpy(), run_oracle(w2))
+
+
+@pytest.mark.parametrize("ps", [1, 16, 48, 64, 100])
+def test_paged_page_sizes(ps):
+    rng = np.random.default_rng(ps)
+    B, L = 5, 9600
+    x = rng.standard_normal((B, L)).astype(np.float32)
+    lens = np.array([9600, 9599, 5000, 1025, 7], dtype=np.int32)
+    npg = (L + ps - 1) // ps
+    pt = np.stack([rng.permutation(npg) + 3 for _ in range(B)]).astype(np.int32)
+    w = _dense("paged", "paged", x, 1024, lens, ps=ps, pt=pt)
+    assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+def test_ragged_small_and_odd():
+    rng = np.random.default_rng(77)
+    lengths = np.array([0, 1, 1023, 1024, 1025, 5001, 32768, 40000, 3], dtype=np.int32)
+    starts = np.zeros_like(lengths)
+    starts[1:] = np.cumsum(lengths[:-1])
+    packed = rng.standard_normal(int(lengths.sum())).astype(np.float32)
+    for k in (1, 1024, 2048):
+        w = Workload("ragged", "ragged", k, lengths.shape[0], packed, row_starts=starts,
+                     lengths=lengths)
+        assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+def test_empty_batch_and_output_stride():
+    d = dev()
+    s = torch.empty((0, 128), dtype=torch.float32, device=d)
+    out = ets.topk_raw(s, 16)
+    assert out.shape == (0, 16)
+    # output rows wider than k: only the first k slots are written
+    x = np.random.default_rng(1).standard_normal((3, 5000)).astype(np.float32)
+    wide = torch.full((3, 1500), 99, dtype=torch.int32, device=d)
+    ets.topk_raw(torch.from_numpy(x).to(d), 1024, out=wide[:, :1024])
+    torch.cuda.synchronize(d)
+    wn = wide.cpu().numpy()
+    assert (wn[:, 1024:] == 99).all()
+    w = _dense("stride", "raw", x, 1024)
+    assert_parity(w, wn[:, :1024], run_oracle(w))
+
+
+def test_invalid_arguments_raise():
+    d = dev()
+    s = torch.zeros((2, 64), dtype=torch.float32, device=d)
+    with pytest.raises(ets.EtsError):
+        ets.topk_raw(s, 0)
+    with pytest.raises(ets.EtsError):
+        ets.topk_raw(s, 4096)
+    with pytest.raises(TypeError):
+        ets.topk_raw(s.double(), 8)
