@@ -1,0 +1,307 @@
+"""Throughput of exact per-row top-k on one MI355X.
+
+One step = one call of the whole path (one kernel launch per batch) over one
+batch of synthetic input already resident in HBM.  The timed K steps are
+captured once into a HIP graph and replayed, so host launch overhead is not
+measured.  Each step reads a different copy of the inputs from a ring of at
+least 512 MiB, so the 256 MiB last-level cache cannot serve the scores.
+
+Prints one JSON line: rows/s (value) plus effective HBM GB/s against the
+8 TB/s peak (roofline) and the CPU oracle's rows/s on the host (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "rows/sec and effective HBM GB/s (% of peak), top-k k=1024/2048, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+RING_BYTES = 512 << 20
+KERNEL_SOURCE = os.path.join(ROOT, "exact_top_selection_amd", "csrc", "ets_topk.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes the method must move per call: each valid score read once, the
+    k outputs written, the length read, the touched page-table entries (paged)
+    or the row start (ragged)."""
+    n = w.row_lengths.astype(np.int64)
+    total = 4 * n + 4 * w.k + 4
+    if w.api == "paged":
+        total += 4 * ((n + w.page_size - 1) // w.page_size)
+    if w.api == "ragged":
+        total += 4
+    return int(total.sum())
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_sha") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The CPU oracle on the host cores over repeated full batches."""
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    oracle.build()
+
+    def once():
+        if w.api == "raw":
+            oracle.topk_raw(w.scores, w.k, w.lens, threads=threads)
+        elif w.api == "paged":
+            oracle.topk_paged(w.scores, w.lens, w.page_table, w.page_size, w.k, threads=threads)
+        else:
+            oracle.topk_ragged(w.scores, w.row_starts, w.lengths, w.k, threads=threads)
+
+    once()  # warm
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        once()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 10000:
+            break
+    rows = reps * w.B
+    return {"value": rows / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full batches of %s (%d rows) in %.1f s, %d threads, %s"
+                      % (reps, w.name, rows, el, threads, platform.processor() or platform.machine())}
+
+
+COPY_BYTES = 256 << 20
+
+
+def calibrate_copy(torch, steps: int) -> int:
+    """A plain device-to-device copy of COPY_BYTES per launch: the reference for
+    scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(max(steps, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": COPY_BYTES, "launches": max(steps, 1)}))
+    return 0
+
+
+def _pmc_per_dispatch(path: str, counter: str, name_part: str):
+    """Mean counter value per dispatch of kernels whose name contains name_part."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter or name_part not in r["Kernel_Name"]:
+                continue
+            vals.setdefault(r["Dispatch_Id"], 0.0)
+            vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not vals:
+        return None, 0
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def traffic_report(d: str, workload: str, seed: int) -> int:
+    """Reads DIR/{fetch,write,copy_fetch,copy_write}/*counter_collection.csv."""
+    import glob
+    import workloads
+
+    def one(sub, counter, part):
+        files = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit("no counter csv under %s/%s" % (d, sub))
+        return _pmc_per_dispatch(files[0], counter, part)
+
+    kf, nkf = one("fetch", "FETCH_SIZE", "row_topk_kernel")
+    kw, nkw = one("write", "WRITE_SIZE", "row_topk_kernel")
+    cf, ncf = one("copy_fetch", "FETCH_SIZE", "copy")
+    cw, ncw = one("copy_write", "WRITE_SIZE", "copy")
+    # counters are in KiB per dispatch; scale each by the copy kernel's reading
+    sf = COPY_BYTES / (cf * 1024.0)
+    sw = COPY_BYTES / (cw * 1024.0)
+    fetch_b = kf * 1024.0 * sf
+    write_b = kw * 1024.0 * sw
+    w = workloads.make(workload, seed=seed)
+    rec = {"kernel_sha": kernel_hash(), "bytes_per_launch": fetch_b + write_b,
+           "fetch_bytes": fetch_b, "write_bytes": write_b,
+           "fetch_kib_raw": kf, "write_kib_raw": kw, "copy_fetch_scale": sf,
+           "copy_write_scale": sw, "algorithmic_bytes": algorithmic_bytes(w),
+           "dispatches": [nkf, nkw, ncf, ncw]}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[w.name] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+    print(json.dumps({w.name: rec}, indent=1))
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="C3", help="C1 .. C5 (default C3)")
+    ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the timed steps one by one instead of replaying a HIP graph")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain device copy of known size (counter calibration) and exit")
+    ap.add_argument("--traffic-report", metavar="DIR",
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE csv runs under DIR into "
+                         "profiles/traffic.json and print a summary (no GPU needed)")
+    args = ap.parse_args()
+    if args.traffic_report:
+        return traffic_report(args.traffic_report, args.workload, args.seed)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the top-k rows are independent and this build "
+              "has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_top_selection_amd as ets
+    import workloads
+
+    if args.calibrate_copy:
+        return calibrate_copy(torch, args.steps)
+
+    w = workloads.make(args.workload, seed=args.seed)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- ring of input copies (>= 512 MiB) resident in HBM
+    per_copy = w.scores.nbytes
+    R = max(1, -(-RING_BYTES // per_copy))
+    scores0 = torch.from_numpy(w.scores).to(dev)
+    ring = torch.empty((R,) + tuple(scores0.shape), dtype=torch.float32, device=dev)
+    ring.copy_(scores0.unsqueeze(0).expand_as(ring))
+    del scores0
+    out = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+    if w.api == "paged":
+        lens = torch.from_numpy(w.lens).to(dev)
+        pt = torch.from_numpy(w.page_table).to(dev)
+
+        def step(i):
+            ets.topk_paged(ring[i % R], lens, pt, out, w.page_size)
+    elif w.api == "raw":
+        lens = torch.from_numpy(w.lens).to(dev) if w.lens is not None else None
+
+        def step(i):
+            ets.topk_raw(ring[i % R], w.k, lens, out=out)
+    else:
+        starts = torch.from_numpy(w.row_starts).to(dev)
+        lengths = torch.from_numpy(w.lengths).to(dev)
+        max_len = w.max_len
+        ws_bytes = ets.workspace_size(w.B, max_len, w.k)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+        def step(i):
+            ets.topk_ragged(ring[i % R], starts, lengths, w.k, max_len=max_len, out=out,
+                            workspace=ws)
+
+    # ---- warmup (eager), then capture the K timed steps into one graph
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        cap_stream = torch.cuda.Stream()
+        cap_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap_stream):
+            with torch.cuda.graph(graph, stream=cap_stream):
+                for i in range(args.steps):
+                    step(args.warmup + i)
+        torch.cuda.current_stream().wait_stream(cap_stream)
+        torch.cuda.synchronize()
+        graph.replay()  # uploads the graph; untimed
+        torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if args.eager:
+        for i in range(args.steps):
+            step(args.warmup + i)
+    else:
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_per_step = ms_total / args.steps
+    rows_per_s = w.B / (ms_per_step * 1e-3)
+    abytes = algorithmic_bytes(w)
+    achieved = abytes / (ms_per_step * 1e-3) / 1e9  # GB/s; one kernel launch per step
+
+    result = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: %s" % (w.name, w.note),
+            "api": w.api, "B": w.B, "L": int(w.L or w.max_len), "k": w.k,
+            "page_size": w.page_size or None, "seed": args.seed,
+            "input_ring_copies": R,
+            "launch": "eager launches" if args.eager else "hip graph of K steps",
+            "algorithmic_bytes_per_step": abytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": measured_traffic(w.name),
+            "kernel": "row_topk_kernel",
+            "kernel_us_per_launch": ms_per_step * 1e3,
+        },
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

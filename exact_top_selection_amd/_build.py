@@ -19,6 +19,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # packed fp32 instructions are disabled for every HIP source of this library
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # LDS histogram atomics are aggregated by hand; keep the compiler from
+    # rewriting them into wave reductions
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 
