@@ -25,6 +25,7 @@
 // Only integer arithmetic touches the scores.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 #include <cstdlib>
@@ -65,26 +66,6 @@ struct Params {
 // (PR #37591 digest, order_key32 excerpt), written branch-free.
 __device__ __forceinline__ uint32_t order_key(uint32_t bits) {
   return bits ^ (static_cast<uint32_t>(static_cast<int32_t>(bits) >> 31) | 0x80000000u);
-}
-
-template <int MODE>
-__device__ __forceinline__ int32_t map_position(const Params& p, const int32_t* pt_row,
-                                                int32_t row_start, int32_t pos) {
-  if constexpr (MODE == kPaged) {
-    int32_t page, slot;
-    if (p.page_shift >= 0) {
-      page = pos >> p.page_shift;
-      slot = pos & (p.page_size - 1);
-    } else {
-      page = pos / p.page_size;
-      slot = pos - page * p.page_size;
-    }
-    return pt_row[page] * p.page_size + slot;
-  } else if constexpr (MODE == kRagged) {
-    return row_start + pos;
-  } else {
-    return pos;
-  }
 }
 
 // ---------------------------------------------------------------- wave / block primitives
@@ -132,27 +113,6 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
   return op(op(readlane(x, 0), readlane(x, 16)), op(readlane(x, 32), readlane(x, 48)));
 }
 
-// Exclusive prefix sum over the block in thread order; `total` gets the sum.
-// Uses s_wave[0 .. T/64); ends with a barrier so s_wave may be reused.
-template <int T>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
-  constexpr int W = T / 64;
-  const int wid = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan(v);
-  if (__lane_id() == 63) s_wave[wid] = incl;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < W; ++w) {
-    const uint32_t s = s_wave[w];
-    tot += s;
-    before += (w < wid) ? s : 0u;
-  }
-  __syncthreads();
-  total = tot;
-  return before + incl - v;
-}
-
 // Adds one to hist[bin] for every lane with `pred` (call in uniform control
 // flow).  Lanes that share lane 0's bin are merged into one LDS atomic issued
 // by lane 0, which removes the serialisation when most of a wave lands in one
@@ -166,13 +126,18 @@ __device__ __forceinline__ void hist_add_peel(uint32_t* hist, bool pred, uint32_
 }
 
 // Finds the histogram bin t with above(t) < kk <= above(t) + hist[t], where
-// above(t) counts the entries of all higher bins.  Every thread gets
-// (t, above(t), hist[t]) in s_res[0..2] after the final barrier.
+// above(t) counts the entries of all higher bins; bin 0 is read as
+// hist[0] - bin0_less.  Two barriers.  Every thread gets (t, above(t),
+// hist[t]) in res[0..2].  wsum[] and res[] may be reused after one more
+// barrier.
 template <int T>
 __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, uint32_t kk,
-                                                   uint32_t* s_wave, uint32_t* s_res) {
+                                                   uint32_t bin0_less, uint32_t* wsum,
+                                                   uint32_t* res) {
   constexpr int BPT = kHistBins / T;  // bins owned by each thread
+  constexpr int W = T / 64;
   static_assert(BPT * T == kHistBins && BPT % 4 == 0, "block size must divide the bins by 4");
+  const int wid = threadIdx.x >> 6;
   uint32_t h[BPT];
   uint32_t s = 0;
 #pragma unroll
@@ -182,24 +147,29 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, uint32_
     h[i + 1] = q.y;
     h[i + 2] = q.z;
     h[i + 3] = q.w;
-    s += q.x + q.y + q.z + q.w;
   }
-  uint32_t total;
-  const uint32_t excl = block_excl_scan<T>(s, s_wave, total);
-  uint32_t above = total - excl - s;  // entries in bins of higher threads
+  if (threadIdx.x == 0) h[0] -= bin0_less;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) s += h[i];
+  const uint32_t incl = wave_incl_scan(s);
+  if (__lane_id() == 63) wsum[wid] = incl;
+  __syncthreads();
+  uint32_t above = readlane(incl, 63) - incl;  // higher lanes of this wave
+#pragma unroll
+  for (int w = 0; w < W; ++w) above += (w > wid) ? wsum[w] : 0u;
 #pragma unroll
   for (int i = BPT - 1; i >= 0; --i) {
     if (above < kk && kk <= above + h[i]) {
-      s_res[0] = threadIdx.x * BPT + i;
-      s_res[1] = above;
-      s_res[2] = h[i];
+      res[0] = threadIdx.x * BPT + i;
+      res[1] = above;
+      res[2] = h[i];
     }
     above += h[i];
   }
   __syncthreads();
 }
 
-// ---------------------------------------------------------------- single-workgroup row kernel
+// ---------------------------------------------------------------- row spans
 
 // key[j] for a lane-varying j, as a binary tree of selects (no scratch).
 template <int PT>
@@ -216,18 +186,9 @@ __device__ __forceinline__ uint32_t select_slot(const uint32_t (&key)[PT], int j
   return v[0];
 }
 
-struct alignas(16) RowSmem {
-  uint32_t hist[kHistBins];    // LDS histogram (16 KiB)
-  int32_t pt[kPtCap];          // staged page-table row (paged map)
-  uint2 cand[kSmallCap];       // threshold bucket: (key, position)
-  uint32_t wave[64];
-  uint32_t res[4];
-  uint32_t ccount;
-};
-
 // Element layout of one tile held by a thread.  V4: float4 v of thread t holds
-// positions 4 (v T + t) + c; scalar: element j of thread t is at j T + t.
-// In both layouts a thread's positions increase with j.
+// positions base + 4 (v T + t) + c; scalar: slot j of thread t is at
+// base + j T + t.  In both layouts a thread's positions increase with j.
 template <int T, bool V4>
 __device__ __forceinline__ int32_t tile_pos(int j) {
   if constexpr (V4) {
@@ -237,43 +198,87 @@ __device__ __forceinline__ int32_t tile_pos(int j) {
   }
 }
 
-// Loads one tile of keys.  Slots at positions >= n get key 0 and are never
-// counted: the passes below correct for them arithmetically (see row_topk).
+// A contiguous span [start, end) of one row, held tile by tile in the
+// caller's key registers.  Slots at positions >= end hold key 0; the passes
+// correct for them arithmetically (they all fall into bin 0 while a key range
+// starts at 0).
 template <int T, int VEC, bool V4>
-__device__ __forceinline__ void load_tile(uint32_t (&key)[4 * VEC], const float* row, int32_t n,
-                                             int64_t cap, int32_t base) {
-  const int32_t tid = static_cast<int32_t>(threadIdx.x);
-  if constexpr (V4) {
+struct Span {
+  static constexpr int PT = 4 * VEC;
+  static constexpr int TILE = T * PT;
+  using Keys = uint32_t[PT];
+  const float* row;  // position 0 of the row (V4: 16-byte aligned, start % 4 == 0)
+  int32_t start, end;
+
+  // key-0 slots visited by one pass over the span (all in its last tile)
+  __device__ uint32_t pad_slots() const {
+    const int32_t len = end - start;
+    const int32_t last = len - ((len - 1) / TILE) * TILE;
+    return static_cast<uint32_t>(TILE - last);
+  }
+  __device__ __forceinline__ void load(Keys& key, int32_t base) const {
+    const int32_t tid = static_cast<int32_t>(threadIdx.x);
+    if constexpr (V4) {
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      const int32_t q = base + 4 * (v * T + tid);
-      if (q + 3 < n) {
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + q));
-        key[4 * v + 0] = order_key(w.x);
-        key[4 * v + 1] = order_key(w.y);
-        key[4 * v + 2] = order_key(w.z);
-        key[4 * v + 3] = order_key(w.w);
-      } else if (q < n) {
+      for (int v = 0; v < VEC; ++v) {
+        const int32_t q = base + 4 * (v * T + tid);
+        if (q + 3 < end) {
+          const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + q));
+          key[4 * v + 0] = order_key(w.x);
+          key[4 * v + 1] = order_key(w.y);
+          key[4 * v + 2] = order_key(w.z);
+          key[4 * v + 3] = order_key(w.w);
+        } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          key[4 * v + c] = (q + c < n) ? order_key(__float_as_uint(row[q + c])) : 0u;
+          for (int c = 0; c < 4; ++c) {
+            key[4 * v + c] = (q + c < end) ? order_key(__float_as_uint(row[q + c])) : 0u;
+          }
         }
-      } else {
+      }
+    } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) key[4 * v + c] = 0u;
+      for (int j = 0; j < PT; ++j) {
+        const int32_t q = base + j * T + tid;
+        key[j] = (q < end) ? order_key(__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row) + q)) : 0u;
       }
     }
-  } else {
+  }
+  // f(key, position, slot) over every slot.  RESIDENT: the span is one tile,
+  // already in key; otherwise every call streams the span again.
+  template <bool RESIDENT, class F>
+  __device__ __forceinline__ void for_each(Keys& key, F&& f) const {
+    if constexpr (!RESIDENT) {
+      for (int32_t base = start; base < end; base += TILE) {
+        load(key, base);
 #pragma unroll
-    for (int j = 0; j < 4 * VEC; ++j) {
-      const int32_t q = base + j * T + tid;
-      key[j] = (q < n) ? order_key(__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row) + q)) : 0u;
+        for (int j = 0; j < PT; ++j) f(key[j], base + tile_pos<T, V4>(j), j);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PT; ++j) f(key[j], start + tile_pos<T, V4>(j), j);
     }
   }
-  (void)cap;
-}
+};
 
-// Clears the histogram (call between barriers).
+// ---------------------------------------------------------------- threshold refinement
+
+// State of the selection: the threshold bucket and what is still needed.
+struct Sel {
+  uint32_t lo, hi;    // key range of the bucket
+  uint32_t kk;        // entries still to take from the bucket
+  uint32_t bucket;    // entries in the bucket (0xFFFFFFFF = not counted yet)
+  uint32_t tie;       // 1: the bucket is one key, narrowed by position
+  uint32_t dlo, dhi;  // tie: range of d = n - 1 - pos in the bucket
+};
+
+struct alignas(16) SelSmem {
+  // double-buffered histogram; the 64 words after each buffer are per-lane
+  // dummy bins that out-of-range lanes add into
+  uint32_t hist[2][kHistBins + 64];
+  uint32_t wsum[16];
+  uint32_t res[4];
+};
+
 template <int T>
 __device__ __forceinline__ void hist_clear(uint32_t* hist) {
 #pragma unroll
@@ -282,33 +287,205 @@ __device__ __forceinline__ void hist_clear(uint32_t* hist) {
   }
 }
 
+// Radix rounds until the bucket holds at most kSmallCap entries: 12-bit
+// rounds on the key inside [lo, hi], then (one key left with too many ties)
+// rounds on d = n - 1 - pos among the scores equal to it, so that the
+// lowest positions win.  Padding slots have pos >= n: their d wraps far
+// above any range.  Round r counts into hist[r & 1] and clears the other
+// buffer.  Precondition: hist[round & 1] is zero and a barrier has passed.
+// Each wave probes (with probe_key) whether its lanes pile into one bin and
+// only then merges its LDS atomics.  Returns the refined state.
+template <int T, class ForEach>
+__device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel in, uint32_t nm1,
+                                      uint32_t n_pad, uint32_t probe_key, int& round) {
+  uint32_t lo = in.lo, hi = in.hi, kk = in.kk, bucket = in.bucket;
+  uint32_t tie = 0, dlo = 0, dhi = nm1;
+  while (bucket > static_cast<uint32_t>(kSmallCap) && lo != hi) {
+    uint32_t* hist = sm.hist[round & 1];
+    hist_clear<T>(sm.hist[(round + 1) & 1]);
+    const uint32_t rlo = lo, span = hi - lo;
+    const int bl = span ? 32 - __clz(static_cast<int>(span)) : 0;
+    const int s = bl > kHistBits ? bl - kHistBits : 0;
+    bool peel;
+    {
+      const uint32_t d = probe_key - rlo;
+      const uint32_t bin = d >> s;
+      const uint32_t lead = readfirstlane(bin);
+      peel = __popcll(__ballot(d <= span && bin == lead)) > kPeelShare;
+    }
+    if (peel) {
+      for_each([&](uint32_t x, int32_t, int) {
+        const uint32_t d = x - rlo;
+        hist_add_peel(hist, d <= span, d >> s);
+      });
+    } else {
+      const uint32_t dummy = kHistBins + __lane_id();
+      for_each([&](uint32_t x, int32_t, int) {
+        const uint32_t d = x - rlo;
+        atomicAdd(&hist[d <= span ? d >> s : dummy], 1u);
+      });
+    }
+    __syncthreads();
+    find_threshold_bin<T>(hist, kk, rlo == 0 ? n_pad : 0u, sm.wsum, sm.res);
+    kk -= sm.res[1];
+    bucket = sm.res[2];
+    lo = rlo + (sm.res[0] << s);
+    const uint32_t width = (1u << s) - 1u;
+    if (hi - lo > width) hi = lo + width;
+    ++round;
+  }
+  if (bucket > static_cast<uint32_t>(kSmallCap)) {
+    tie = 1;
+    const uint32_t tkey = lo;
+    while (bucket > static_cast<uint32_t>(kSmallCap)) {
+      uint32_t* hist = sm.hist[round & 1];
+      hist_clear<T>(sm.hist[(round + 1) & 1]);
+      const uint32_t rdlo = dlo, span = dhi - dlo;
+      const int bl = span ? 32 - __clz(static_cast<int>(span)) : 0;
+      const int s = bl > kHistBits ? bl - kHistBits : 0;
+      for_each([&](uint32_t x, int32_t pos, int) {
+        const uint32_t d = nm1 - static_cast<uint32_t>(pos) - rdlo;
+        if (x == tkey && d <= span) atomicAdd(&hist[d >> s], 1u);
+      });
+      __syncthreads();
+      find_threshold_bin<T>(hist, kk, 0u, sm.wsum, sm.res);
+      kk -= sm.res[1];
+      bucket = sm.res[2];
+      dlo = rdlo + (sm.res[0] << s);
+      const uint32_t width = (1u << s) - 1u;
+      if (dhi - dlo > width) dhi = dlo + width;
+      ++round;
+    }
+  }
+  Sel out;
+  out.lo = lo;
+  out.hi = hi;
+  out.kk = kk;
+  out.bucket = bucket;
+  out.tie = tie;
+  out.dlo = dlo;
+  out.dhi = dhi;
+  return out;
+}
+
+// Winner: key above the bucket, or (tie) the bucket's key at a lower
+// position than the bucket.  Bucket member: the rest of the bucket.  Slots
+// at positions >= end are padding (key 0): they can only match when the
+// bucket reaches key 0, so those cases check the position.
+__device__ __forceinline__ bool sel_winner(const Sel& s, uint32_t nm1, int32_t end, uint32_t x,
+                                           int32_t pos) {
+  if (!s.tie) return x > s.hi;
+  const uint32_t d = nm1 - static_cast<uint32_t>(pos);
+  return x > s.hi || (x == s.hi && d > s.dhi && pos < end);
+}
+__device__ __forceinline__ bool sel_bucket(const Sel& s, uint32_t nm1, int32_t end, uint32_t x,
+                                           int32_t pos) {
+  if (!s.tie) return x - s.lo <= s.hi - s.lo && (s.lo != 0 || pos < end);
+  return x == s.hi && nm1 - static_cast<uint32_t>(pos) - s.dlo <= s.dhi - s.dlo &&
+         (s.hi != 0 || pos < end);
+}
+
+// Output value of selected position pos of a row.
+template <int MODE>
+__device__ __forceinline__ int32_t out_value(const Params& p, const int32_t* pt_lds,
+                                             const int32_t* pt_row, int32_t row_start, int32_t pos) {
+  if constexpr (MODE == kPaged) {
+    int32_t page, off;
+    if (p.page_shift >= 0) {
+      page = pos >> p.page_shift;
+      off = pos & (p.page_size - 1);
+    } else {
+      page = pos / p.page_size;
+      off = pos - page * p.page_size;
+    }
+    return (pt_lds ? pt_lds[page] : pt_row[page]) * p.page_size + off;
+  } else if constexpr (MODE == kRagged) {
+    return row_start + pos;
+  } else {
+    return pos;
+  }
+}
+
+// Ranks up to kSmallCap bucket entries on (key desc, position asc) and emits
+// the kk best at slots first + rank.  Eight lanes share an entry: each
+// compares it with every eighth entry, then row permutes sum the counts.
+template <int T, class Emit>
+__device__ __forceinline__ void rank_bucket(const uint2* cand, uint32_t nc, uint32_t kk,
+                                            uint32_t first, Emit&& emit) {
+  static_assert(T >= 8 * kSmallCap, "eight lanes per bucket entry");
+  const uint32_t i = threadIdx.x >> 3;
+  const uint32_t part = threadIdx.x & 7;
+  uint32_t rank = 0;
+  uint2 ci = make_uint2(0, 0);
+  if (i < nc) {
+    ci = cand[i];
+#pragma unroll
+    for (uint32_t q = 0; q < kSmallCap / 8; ++q) {
+      const uint32_t j = part + 8 * q;
+      const uint2 cj = cand[min(j, nc - 1)];
+      const bool before = cj.x > ci.x || (cj.x == ci.x && static_cast<int32_t>(cj.y) < static_cast<int32_t>(ci.y));
+      rank += (j < nc && before) ? 1u : 0u;
+    }
+  }
+  rank += dpp_perm<0xB1>(rank);   // quad_perm [1,0,3,2]
+  rank += dpp_perm<0x4E>(rank);   // quad_perm [2,3,0,1]
+  rank += dpp_perm<0x141>(rank);  // row_half_mirror: the other quad of the eight
+  if (i < nc && part == 0 && rank < kk) emit(first + rank, static_cast<int32_t>(ci.y));
+}
+
+// Row geometry shared by every kernel: valid length, base pointer, offsets.
+template <int MODE>
+struct RowRef {
+  int32_t n;
+  int32_t row_start;
+  const float* row;
+  const int32_t* pt_row;
+  int32_t* out;
+  __device__ RowRef(const Params& p, int b) {
+    row_start = 0;
+    if constexpr (MODE == kRagged) {
+      row_start = p.row_starts[b];
+      n = max(p.lens[b], 0);
+      row = p.scores + row_start;
+    } else {
+      n = p.lens ? min(max(p.lens[b], 0), p.L) : p.L;
+      row = p.scores + static_cast<int64_t>(b) * p.row_stride;
+    }
+    pt_row = (MODE == kPaged) ? p.page_table + static_cast<int64_t>(b) * p.pt_stride : nullptr;
+    out = p.out + static_cast<int64_t>(b) * p.out_stride;
+  }
+};
+
+// Rows no longer than k: every position is selected, the rest is padding.
+template <int T, int MODE>
+__device__ __forceinline__ void emit_whole_row(const Params& p, const RowRef<MODE>& r) {
+  for (int32_t i = threadIdx.x; i < p.k; i += T) {
+    r.out[i] = (i < r.n) ? out_value<MODE>(p, nullptr, r.pt_row, r.row_start, i) : -1;
+  }
+}
+
+// ---------------------------------------------------------------- single-workgroup row kernel
+
+struct alignas(16) RowSmem {
+  SelSmem sel;
+  int32_t pt[kPtCap];     // staged page-table row (paged map)
+  uint2 cand[kSmallCap];  // threshold bucket: (key, position)
+  uint32_t red[64];       // per-wave partials (bounds)
+  uint32_t ccount;
+};
+
 // One exact top-k row on one workgroup.  STREAM = false: the row (n <= one
 // tile) is loaded once and every pass runs on registers.  STREAM = true: any
-// length; every pass streams the row tile by tile.
-//
-// Slots beyond the row hold key 0.  They can only matter while the key range
-// starts at 0, where all of them fall into bin 0: that bin is corrected by
-// their known count, and the passes that emit positions check pos < n.
+// length; every pass streams the row tile by tile (L2 after the first).
 template <int T, int VEC, int MODE, bool V4, bool STREAM>
-__device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, int32_t n, const float* row,
-                                         int64_t cap, int32_t row_start, const int32_t* pt_row,
-                                         int32_t* out) {
-  constexpr int PT = 4 * VEC;
-  constexpr int TILE = T * PT;
+__device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const RowRef<MODE>& r) {
+  using SpanT = Span<T, VEC, V4>;
+  constexpr int PT = SpanT::PT;
   constexpr int W = T / 64;
   const int tid = threadIdx.x;
   const int wid = tid >> 6;
   const int32_t k = p.k;
-  // Slots a thread uses in a tile of nt scores: whole float4 groups (V4) or
-  // whole strides (scalar) that hold at least one score.  Uniform per block.
-  auto slots_for = [](int32_t nt) -> int32_t {
-    return V4 ? min(4 * ((nt + 4 * T - 1) / (4 * T)), PT) : min((nt + T - 1) / T, PT);
-  };
-  const int32_t ntiles = STREAM ? (n + TILE - 1) / TILE : 1;
-  const int32_t last_n = n - (ntiles - 1) * TILE;  // scores in the last tile
-  const int32_t jlim = slots_for(last_n);           // resident rows: used slots
-  // key-0 slots inside the used slots (only the last tile has any)
-  const uint32_t n_pad = static_cast<uint32_t>(jlim * T - last_n);
+  const int32_t n = r.n;
 
   // Page-table row into LDS: issued before the score loads so its latency
   // hides behind them.
@@ -321,13 +498,17 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, int32_t n
     pt_lds = npages <= kPtCap;
     if (pt_lds) {
 #pragma unroll
-      for (int i = 0; i < PTV; ++i) ptv[i] = (tid + i * T < npages) ? pt_row[tid + i * T] : 0;
+      for (int i = 0; i < PTV; ++i) ptv[i] = (tid + i * T < npages) ? r.pt_row[tid + i * T] : 0;
     }
   }
 
+  const SpanT span{r.row, 0, n};
   uint32_t key[PT];
-  if constexpr (!STREAM) load_tile<T, VEC, V4>(key, row, n, cap, 0);
+  if constexpr (!STREAM) span.load(key, 0);
+  auto for_each = [&](auto&& f) { span.template for_each<!STREAM>(key, f); };
 
+  hist_clear<T>(sm.sel.hist[0]);
+  if (tid == 0) sm.ccount = 0;
   if constexpr (MODE == kPaged) {
     if (pt_lds) {
 #pragma unroll
@@ -335,24 +516,6 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, int32_t n
         if (tid + i * T < npages) sm.pt[tid + i * T] = ptv[i];
     }
   }
-
-  // f(key, position) over every used slot of the row this thread holds;
-  // slots past the row's end are skipped block-uniformly.
-  auto for_each = [&](auto&& f) {
-    if constexpr (STREAM) {
-      for (int32_t base = 0; base < n; base += TILE) {
-        load_tile<T, VEC, V4>(key, row, n, cap, base);
-        const int32_t jl = slots_for(n - base);
-#pragma unroll
-        for (int j = 0; j < PT; ++j)
-          if (j < jl) f(key[j], base + tile_pos<T, V4>(j));
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < PT; ++j)
-        if (j < jlim) f(key[j], tile_pos<T, V4>(j));
-    }
-  };
 
   // ---- bounds: row max and a lower bound of the k-th largest key.  Each
   // thread's jth-largest key, over the nfull threads that hold at least jth
@@ -362,261 +525,126 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, int32_t n
   const int32_t holders = V4 ? min(T, (n + 3) / 4) : min(T, n);
   const int32_t jth = (k + holders - 1) / holders;
   uint32_t m1 = 0, m2 = 0;
-  for_each([&](uint32_t x, int32_t) {
-    m2 = max(m2, min(m1, x));
-    m1 = max(m1, x);
-  });
-  uint32_t lo, hi;
+  if (jth == 1) {
+    for_each([&](uint32_t x, int32_t, int) { m1 = max(m1, x); });
+    m2 = m1;
+  } else {
+    for_each([&](uint32_t x, int32_t, int) {
+      m2 = max(m2, min(m1, x));
+      m1 = max(m1, x);
+    });
+  }
+  // threads whose first jth slots hold scores (V4: positions 4t .. 4t+jth-1,
+  // scalar: t and t + T)
+  const int32_t jpos = V4 ? 4 * tid + jth - 1 : (jth - 1) * T + tid;
+  const bool full = jth <= 2 && jpos < n;
+  const int32_t nfull = jth > 2 ? 0 : (V4 ? min(T, max(0, (n - jth) / 4 + 1)) : min(T, max(0, n - (jth - 1) * T)));
+  Sel sel0{};
   {
-    // this thread's first jth slots are positions 4 tid .. (V4) or tid, tid + T (scalar)
-    const int32_t jpos = V4 ? 4 * tid + jth - 1 : (jth - 1) * T + tid;
-    const bool full = jth <= 2 && jpos < n;
     const uint32_t rmax = wave_reduce(m1, OpMax());
-    const uint32_t bmin = wave_reduce(full ? (jth == 1 ? m1 : m2) : 0xFFFFFFFFu, OpMin());
-    const uint32_t nfull = wave_reduce(full ? 1u : 0u, OpAdd());
+    const uint32_t bmin = wave_reduce(full ? m2 : 0xFFFFFFFFu, OpMin());
     if (__lane_id() == 0) {
-      sm.wave[wid] = rmax;
-      sm.wave[16 + wid] = bmin;
-      sm.wave[32 + wid] = nfull;
+      sm.red[wid] = rmax;
+      sm.red[16 + wid] = bmin;
     }
     __syncthreads();
-    uint32_t gmax = 0, gb = 0xFFFFFFFFu, gfull = 0;
+    uint32_t gmax = 0, gb = 0xFFFFFFFFu;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      gmax = max(gmax, sm.wave[w]);
-      gb = min(gb, sm.wave[16 + w]);
-      gfull += sm.wave[32 + w];
+      gmax = max(gmax, sm.red[w]);
+      gb = min(gb, sm.red[16 + w]);
     }
-    __syncthreads();
-    hi = gmax;
-    if (jth <= 2 && gfull * static_cast<uint32_t>(jth) >= static_cast<uint32_t>(k)) {
-      lo = gb;
+    sel0.hi = gmax;
+    if (nfull * jth >= k) {
+      sel0.lo = gb;
     } else {
       uint32_t mn = 0xFFFFFFFFu;
-      for_each([&](uint32_t x, int32_t pos) { mn = min(mn, pos < n ? x : 0xFFFFFFFFu); });
+      for_each([&](uint32_t x, int32_t pos, int) { mn = min(mn, pos < n ? x : 0xFFFFFFFFu); });
       mn = wave_reduce(mn, OpMin());
-      if (__lane_id() == 0) sm.wave[wid] = mn;
+      if (__lane_id() == 0) sm.red[32 + wid] = mn;
       __syncthreads();
-      lo = 0xFFFFFFFFu;
+      sel0.lo = 0xFFFFFFFFu;
 #pragma unroll
-      for (int w = 0; w < W; ++w) lo = min(lo, sm.wave[w]);
-      __syncthreads();
+      for (int w = 0; w < W; ++w) sel0.lo = min(sel0.lo, sm.red[32 + w]);
     }
   }
+  sel0.kk = static_cast<uint32_t>(k);
+  sel0.bucket = 0xFFFFFFFFu;
 
-  // ---- radix rounds on the key inside [lo, hi] until the threshold bucket is
-  // small, or a single key.  Each round first probes how many lanes of a wave
-  // share one bin; only then is the merging (peeled) LDS atomic worth its cost.
-  uint32_t kk = static_cast<uint32_t>(k);
-  uint32_t bucket = 0;
-  for (;;) {
-    const uint32_t span = hi - lo;
-    const int bl = span ? 32 - __clz(static_cast<int>(span)) : 0;
-    const int s = bl > kHistBits ? bl - kHistBits : 0;
-    {
-      const uint32_t d = key[0] - lo;
-      const uint32_t bin = d >> s;
-      const uint32_t lead = readfirstlane(bin);
-      const uint32_t share = static_cast<uint32_t>(__popcll(__ballot(d <= span && bin == lead)));
-      if (__lane_id() == 0) sm.wave[48 + wid] = share;
-    }
-    hist_clear<T>(sm.hist);
-    __syncthreads();
-    uint32_t max_share = 0;
-#pragma unroll
-    for (int w = 0; w < W; ++w) max_share = max(max_share, sm.wave[48 + w]);
-    if (max_share > kPeelShare) {
-      for_each([&](uint32_t x, int32_t) {
-        const uint32_t d = x - lo;
-        hist_add_peel(sm.hist, d <= span, d >> s);
-      });
-    } else {
-      for_each([&](uint32_t x, int32_t) {
-        const uint32_t d = x - lo;
-        if (d <= span) atomicAdd(&sm.hist[d >> s], 1u);
-      });
-    }
-    __syncthreads();
-    if (lo == 0) {
-      if (tid == 0) sm.hist[0] -= n_pad;
-      __syncthreads();
-    }
-    find_threshold_bin<T>(sm.hist, kk, sm.wave, sm.res);
-    const uint32_t t = sm.res[0];
-    kk -= sm.res[1];
-    bucket = sm.res[2];
-    lo += t << s;
-    const uint32_t width = (1u << s) - 1u;
-    if (hi - lo > width) hi = lo + width;
-    __syncthreads();  // sm.res is rewritten by the next round
-    if (bucket <= static_cast<uint32_t>(kSmallCap) || s == 0) break;
-  }
-
-  // ---- a single key with too many ties: radix rounds on d = n - 1 - pos
-  // among the scores equal to it (the largest d is the lowest position).
-  // Padding slots have pos >= n, so their d wraps far above any range.
-  // Positions are distinct, so these histograms never pile onto one bin.
-  const bool tie_stage = bucket > static_cast<uint32_t>(kSmallCap);
-  uint32_t dlo = 0, dhi = static_cast<uint32_t>(n - 1);
+  // ---- radix refinement until the bucket is small
   const uint32_t nm1 = static_cast<uint32_t>(n - 1);
-  if (tie_stage) {
-    const uint32_t tkey = lo;
-    for (;;) {
-      const uint32_t span = dhi - dlo;
-      const int bl = span ? 32 - __clz(static_cast<int>(span)) : 0;
-      const int sd = bl > kHistBits ? bl - kHistBits : 0;
-      hist_clear<T>(sm.hist);
-      __syncthreads();
-      for_each([&](uint32_t x, int32_t pos) {
-        const uint32_t d = nm1 - static_cast<uint32_t>(pos) - dlo;
-        if (x == tkey && d <= span) atomicAdd(&sm.hist[d >> sd], 1u);
-      });
-      __syncthreads();
-      find_threshold_bin<T>(sm.hist, kk, sm.wave, sm.res);
-      const uint32_t t = sm.res[0];
-      kk -= sm.res[1];
-      bucket = sm.res[2];
-      dlo += t << sd;
-      const uint32_t width = (1u << sd) - 1u;
-      if (dhi - dlo > width) dhi = dlo + width;
-      __syncthreads();
-      if (bucket <= static_cast<uint32_t>(kSmallCap)) break;
-    }
-  }
+  int round = 0;
+  const Sel sel = refine<T>(for_each, sm.sel, sel0, nm1, span.pad_slots(), key[0], round);
 
-  // Winners: key above the bucket, or (tie stage) the bucket's key at a
-  // lower position than the bucket.  Bucket: the remaining candidates.
-  const uint32_t klo = lo, khi = hi, kspan = hi - lo, dspan = dhi - dlo;
-  // output value of a selected position
+  // ---- scatter: append the bucket to LDS, count the winners, place them by
+  // one block scan (whose barrier also publishes the bucket), emit them.
+  const uint32_t first = static_cast<uint32_t>(k) - sel.kk;  // number of winners
+  const int32_t* pt_stage = pt_lds ? sm.pt : nullptr;
   auto emit = [&](uint32_t slot, int32_t pos) {
-    int32_t v;
-    if constexpr (MODE == kPaged) {
-      int32_t page, off;
-      if (p.page_shift >= 0) {
-        page = pos >> p.page_shift;
-        off = pos & (p.page_size - 1);
-      } else {
-        page = pos / p.page_size;
-        off = pos - page * p.page_size;
-      }
-      v = (pt_lds ? sm.pt[page] : pt_row[page]) * p.page_size + off;
-    } else if constexpr (MODE == kRagged) {
-      v = row_start + pos;
-    } else {
-      v = pos;
-    }
-    out[slot] = v;
+    r.out[slot] = out_value<MODE>(p, pt_stage, r.pt_row, r.row_start, pos);
   };
-
-  if (tid == 0) sm.ccount = 0;
-  __syncthreads();
-  // Count winners, gather the bucket into LDS (rare: skipped per wave), and
-  // emit the winners in thread order.  TIE selects the tie-stage tests.
-  auto scatter = [&](auto tie_tag) -> uint32_t {
-    constexpr bool TIE = decltype(tie_tag)::value;
-    auto is_winner = [&](uint32_t x, int32_t pos) {
-      if constexpr (!TIE) {
-        return x > khi;
-      } else {
-        const uint32_t d = nm1 - static_cast<uint32_t>(pos);
-        return x > khi || (x == khi && d > dhi && d <= nm1);
-      }
-    };
-    auto in_bucket = [&](uint32_t x, int32_t pos) {
-      if constexpr (!TIE) {
-        return x - klo <= kspan && pos < n;
-      } else {
-        return x == khi && nm1 - static_cast<uint32_t>(pos) - dlo <= dspan;
-      }
-    };
-    auto gather = [&](uint32_t x, int32_t pos) {
-      const bool c = in_bucket(x, pos);
-      if (__ballot(c) != 0 && c) {
-        const uint32_t slot = atomicAdd(&sm.ccount, 1u);
-        if (slot < static_cast<uint32_t>(kSmallCap)) sm.cand[slot] = make_uint2(x, static_cast<uint32_t>(pos));
-      }
-    };
-    const uint32_t first = static_cast<uint32_t>(k) - kk;  // number of winners
-    if constexpr (!STREAM) {
-      // bit j of wmask / cmask: slot j is a winner / a bucket candidate.  One
-      // block scan of (winners | candidates << 16) places both, in thread order.
-      uint32_t wmask = 0, cmask = 0;
-#pragma unroll
-      for (int j = 0; j < PT; ++j) {
-        if (j < jlim) {
-          const int32_t pos = tile_pos<T, V4>(j);
-          wmask |= (is_winner(key[j], pos) ? 1u : 0u) << j;
-          cmask |= (in_bucket(key[j], pos) ? 1u : 0u) << j;
-        }
-      }
-      const uint32_t packed = static_cast<uint32_t>(__popc(wmask)) |
-                              (static_cast<uint32_t>(__popc(cmask)) << 16);
-      uint32_t total;
-      const uint32_t excl = block_excl_scan<T>(packed, sm.wave, total);  // ends with a barrier
-      uint32_t off = excl & 0xFFFFu;
-      uint32_t coff = excl >> 16;
-      if (tid == 0) sm.ccount = total >> 16;
+  auto append = [&](uint32_t x, int32_t pos) {
+    const uint32_t slot = atomicAdd(&sm.ccount, 1u);
+    if (slot < static_cast<uint32_t>(kSmallCap)) sm.cand[slot] = make_uint2(x, static_cast<uint32_t>(pos));
+  };
+  if constexpr (!STREAM) {
+    uint32_t wmask = 0, cmask = 0;  // bit j: slot j is a winner / in the bucket
+    if (!sel.tie) {
+      const uint32_t khi = sel.hi;
+      for_each([&](uint32_t x, int32_t pos, int j) {
+        wmask |= (x > khi ? 1u : 0u) << j;
+        cmask |= (sel_bucket(sel, nm1, n, x, pos) ? 1u : 0u) << j;
+      });
+    } else {
+      for_each([&](uint32_t x, int32_t pos, int j) {
+        wmask |= (sel_winner(sel, nm1, span.end, x, pos) ? 1u : 0u) << j;
+        cmask |= (sel_bucket(sel, nm1, n, x, pos) ? 1u : 0u) << j;
+      });
+    }
+    if (__ballot(cmask != 0) != 0) {
       while (cmask != 0) {
         const int j = __ffs(static_cast<int>(cmask)) - 1;
         cmask &= cmask - 1u;
-        const int32_t pos = V4 ? 4 * ((j >> 2) * T + tid) + (j & 3) : j * T + tid;
-        if (coff < static_cast<uint32_t>(kSmallCap))
-          sm.cand[coff] = make_uint2(select_slot<PT>(key, j), static_cast<uint32_t>(pos));
-        ++coff;
+        append(select_slot<PT>(key, j), tile_pos<T, V4>(j));
       }
-      __syncthreads();  // candidates visible; no global store is pending here
-      // winners straight to the output; the bound only guards a broken invariant
-      while (wmask != 0) {
-        const int j = __ffs(static_cast<int>(wmask)) - 1;
-        wmask &= wmask - 1u;
-        const int32_t pos = V4 ? 4 * ((j >> 2) * T + tid) + (j & 3) : j * T + tid;
+    }
+    const uint32_t nwin = static_cast<uint32_t>(__popc(wmask));
+    const uint32_t incl = wave_incl_scan(nwin);
+    if (__lane_id() == 63) sm.sel.wsum[wid] = incl;
+    __syncthreads();
+    uint32_t off = incl - nwin;
+#pragma unroll
+    for (int w = 0; w < W; ++w) off += (w < wid) ? sm.sel.wsum[w] : 0u;
+    // the bound only guards the row against a broken invariant
+    while (wmask != 0) {
+      const int j = __ffs(static_cast<int>(wmask)) - 1;
+      wmask &= wmask - 1u;
+      if (off < first) emit(off, tile_pos<T, V4>(j));
+      ++off;
+    }
+  } else {
+    uint32_t nwin = 0;
+    for_each([&](uint32_t x, int32_t pos, int) {
+      nwin += sel_winner(sel, nm1, span.end, x, pos) ? 1u : 0u;
+      const bool c = sel_bucket(sel, nm1, n, x, pos);
+      if (__ballot(c) != 0 && c) append(x, pos);
+    });
+    const uint32_t incl = wave_incl_scan(nwin);
+    if (__lane_id() == 63) sm.sel.wsum[wid] = incl;
+    __syncthreads();
+    uint32_t off = incl - nwin;
+#pragma unroll
+    for (int w = 0; w < W; ++w) off += (w < wid) ? sm.sel.wsum[w] : 0u;
+    for_each([&](uint32_t x, int32_t pos, int) {
+      if (sel_winner(sel, nm1, span.end, x, pos)) {
         if (off < first) emit(off, pos);
         ++off;
       }
-    } else {
-      uint32_t nwin = 0;
-      for_each([&](uint32_t x, int32_t pos) {
-        nwin += is_winner(x, pos) ? 1u : 0u;
-        gather(x, pos);
-      });
-      uint32_t total_win;
-      uint32_t off = block_excl_scan<T>(nwin, sm.wave, total_win);  // ends with a barrier
-      for_each([&](uint32_t x, int32_t pos) {
-        if (is_winner(x, pos)) {
-          if (off < first) emit(off, pos);
-          ++off;
-        }
-      });
-    }
-    return first;
-  };
-  const uint32_t first = tie_stage ? scatter(std::true_type()) : scatter(std::false_type());
-
-  // ---- the bucket's best kk, placed by rank.  Eight lanes share a
-  // candidate: each compares it with every eighth entry, then the lanes'
-  // counts are summed with row permutes.
-  {
-    const uint32_t nc = min(sm.ccount, static_cast<uint32_t>(kSmallCap));
-    static_assert(T >= 8 * kSmallCap, "eight lanes per bucket entry");
-    const uint32_t i = tid >> 3;
-    const uint32_t part = tid & 7;
-    uint32_t rank = 0;
-    uint2 ci = make_uint2(0, 0);
-    if (i < nc) {
-      ci = sm.cand[i];
-#pragma unroll
-      for (uint32_t q = 0; q < kSmallCap / 8; ++q) {
-        const uint32_t j = part + 8 * q;
-        const uint2 cj = sm.cand[min(j, nc - 1)];
-        const bool before = cj.x > ci.x || (cj.x == ci.x && static_cast<int32_t>(cj.y) < static_cast<int32_t>(ci.y));
-        rank += (j < nc && before) ? 1u : 0u;
-      }
-    }
-    rank += dpp_perm<0xB1>(rank);   // quad_perm [1,0,3,2]
-    rank += dpp_perm<0x4E>(rank);   // quad_perm [2,3,0,1]
-    rank += dpp_perm<0x141>(rank);  // row_half_mirror: the other quad of the eight
-    if (i < nc && part == 0 && rank < kk) emit(first + rank, static_cast<int32_t>(ci.y));
+    });
   }
+
+  // ---- the bucket's best kk, placed by rank
+  rank_bucket<T>(sm.cand, min(sm.ccount, static_cast<uint32_t>(kSmallCap)), sel.kk, first, emit);
 }
 
 // One workgroup per row.  STREAM = false: rows fit one tile (the host
@@ -626,44 +654,373 @@ template <int T, int VEC, int MODE, bool V4, bool STREAM>
 __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
   constexpr int TILE = T * 4 * VEC;
   __shared__ RowSmem sm;
-  const int b = blockIdx.x;
-
-  int32_t n;
-  int32_t row_start = 0;
-  int64_t cap;  // readable scores from the row base
-  const float* row;
-  if constexpr (MODE == kRagged) {
-    row_start = p.row_starts[b];
-    n = max(p.lens[b], 0);
-    row = p.scores + row_start;
-    cap = n;
-  } else {
-    n = p.lens ? min(max(p.lens[b], 0), p.L) : p.L;
-    row = p.scores + static_cast<int64_t>(b) * p.row_stride;
-    cap = p.L;
-  }
-  const int32_t* pt_row = nullptr;
-  if constexpr (MODE == kPaged) pt_row = p.page_table + static_cast<int64_t>(b) * p.pt_stride;
-  int32_t* out = p.out + static_cast<int64_t>(b) * p.out_stride;
-
-  if (n <= p.k) {
-    // every position is selected, the rest is padding
-    for (int32_t i = threadIdx.x; i < p.k; i += T) {
-      out[i] = (i < n) ? map_position<MODE>(p, pt_row, row_start, i) : -1;
-    }
+  const RowRef<MODE> r(p, blockIdx.x);
+  if (r.n <= p.k) {
+    emit_whole_row<T, MODE>(p, r);
     return;
   }
   if constexpr (STREAM) {
-    row_topk<T, VEC, MODE, V4, true>(p, sm, n, row, cap, row_start, pt_row, out);
+    row_topk<T, VEC, MODE, V4, true>(p, sm, r);
   } else {
     if constexpr (MODE == kRagged) {
-      if (n > TILE) {
-        row_topk<T, VEC, MODE, V4, true>(p, sm, n, row, cap, row_start, pt_row, out);
+      if (r.n > TILE) {
+        row_topk<T, VEC, MODE, V4, true>(p, sm, r);
         return;
       }
     }
-    row_topk<T, VEC, MODE, V4, false>(p, sm, n, row, cap, row_start, pt_row, out);
+    row_topk<T, VEC, MODE, V4, false>(p, sm, r);
   }
+}
+
+// ---------------------------------------------------------------- row-split path
+//
+// Long rows are cut into G chunks of `chunk` scores, one workgroup each
+// (after the pages' row-split path, PR #37591 topk.hip excerpt: histogram,
+// scatter and refine kernels over a workspace, the kernel boundaries acting
+// as the barriers between the chunks of a row).  Six launches:
+//   split_zero     clears the per-row records and histograms;
+//   split_bounds   per chunk: max, min of lane maxima, holders, min;
+//   split_hist     per chunk: the row's range from all chunks' bounds, a LDS
+//                  histogram of the chunk, merged into the row's histogram;
+//   split_select   per row: the threshold bin; a bucket still above
+//                  kSmallCap is refined by this workgroup streaming the row;
+//   split_scatter  per chunk: winners to the output and the bucket to the
+//                  workspace, placed through one 64-bit cursor per row;
+//   split_finish   per row: rank the bucket, emit; rows with n <= k.
+// Workspace (u32 words): rec[B][16] | part[B][G][4] | hist[B][4096] | cand[B][kSmallCap][2].
+
+constexpr int kRec = 16;
+enum RecField : int { kRecLo = 0, kRecHi, kRecKk, kRecTie, kRecDlo, kRecDhi, kRecShift, kRecPad,
+                      kRecCursor = 8 /* u64: winners << 32 | bucket entries */ };
+
+struct SplitWs {
+  uint32_t* rec;
+  uint32_t* part;
+  uint32_t* hist;
+  uint2* cand;
+  __device__ SplitWs(uint32_t* ws, int32_t B, int32_t G) {
+    rec = ws;
+    part = rec + static_cast<int64_t>(B) * kRec;
+    hist = part + static_cast<int64_t>(B) * G * 4;
+    cand = reinterpret_cast<uint2*>(hist + static_cast<int64_t>(B) * kHistBins);
+  }
+};
+
+__global__ __launch_bounds__(256) void split_zero(uint32_t* ws, int32_t B, int32_t G) {
+  const SplitWs w(ws, B, G);
+  const int64_t nrec = static_cast<int64_t>(B) * kRec;
+  const int64_t nhist = static_cast<int64_t>(B) * kHistBins;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < nrec + nhist; i += 256ll * gridDim.x) {
+    if (i < nrec) w.rec[i] = 0u;
+    else w.hist[i - nrec] = 0u;
+  }
+}
+
+// Chunk g of a row: [g chunk, (g+1) chunk), the last chunk running to the
+// row's end (a ragged row may be longer than the length hint).
+__device__ __forceinline__ int32_t chunk_end(int32_t g, int32_t G, int32_t chunk, int32_t n) {
+  return g == G - 1 ? n : min(g * chunk + chunk, n);
+}
+
+// Runs body(std::true_type) when the span fits one tile (loaded once, kept
+// in registers), else body(std::false_type) (streamed per pass).
+template <class SpanT, class Body>
+__device__ __forceinline__ void with_span(const SpanT& span, typename SpanT::Keys& key, Body&& body) {
+  if (span.end - span.start <= SpanT::TILE) {
+    span.load(key, span.start);
+    body(std::true_type());
+  } else {
+    body(std::false_type());
+  }
+}
+
+template <int T, int VEC, int MODE, bool V4>
+__global__ __launch_bounds__(T) void split_bounds(Params p, uint32_t* ws, int32_t B, int32_t G,
+                                                  int32_t chunk) {
+  constexpr int W = T / 64;
+  __shared__ uint32_t red[4 * 16];
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const RowRef<MODE> r(p, b);
+  if (r.n <= p.k) return;
+  const SplitWs w(ws, B, G);
+  uint32_t* part = w.part + (static_cast<int64_t>(b) * G + g) * 4;
+  const Span<T, VEC, V4> span{r.row, g * chunk, chunk_end(g, G, chunk, r.n)};
+  uint32_t key[4 * VEC];
+  if (span.start >= span.end) {
+    if (threadIdx.x == 0) {
+      part[0] = 0u;
+      part[1] = 0xFFFFFFFFu;
+      part[2] = 0u;
+      part[3] = 0xFFFFFFFFu;
+    }
+    return;
+  }
+  uint32_t m1 = 0, mn = 0xFFFFFFFFu;
+  with_span(span, key, [&](auto res) {
+    span.template for_each<decltype(res)::value>(key, [&](uint32_t x, int32_t pos, int) {
+      m1 = max(m1, x);
+      mn = min(mn, pos < span.end ? x : 0xFFFFFFFFu);
+    });
+  });
+  // a thread holds a score iff its first slot does
+  const int32_t first_pos = span.start + (V4 ? 4 * static_cast<int32_t>(threadIdx.x) : static_cast<int32_t>(threadIdx.x));
+  const bool holds = first_pos < span.end;
+  const uint32_t vmax = wave_reduce(m1, OpMax());
+  const uint32_t vmm = wave_reduce(holds ? m1 : 0xFFFFFFFFu, OpMin());
+  const uint32_t vh = wave_reduce(holds ? 1u : 0u, OpAdd());
+  const uint32_t vmin = wave_reduce(mn, OpMin());
+  const int wid = threadIdx.x >> 6;
+  if (__lane_id() == 0) {
+    red[wid] = vmax;
+    red[16 + wid] = vmm;
+    red[32 + wid] = vh;
+    red[48 + wid] = vmin;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0, bm = 0xFFFFFFFFu, c = 0, d = 0xFFFFFFFFu;
+    for (int i = 0; i < W; ++i) {
+      a = max(a, red[i]);
+      bm = min(bm, red[16 + i]);
+      c += red[32 + i];
+      d = min(d, red[48 + i]);
+    }
+    part[0] = a;
+    part[1] = bm;
+    part[2] = c;
+    part[3] = d;
+  }
+}
+
+// The row's key range from all chunks: [lower bound, max].  The lanes'
+// maxima over all chunks are `holders` distinct scores, so if they number at
+// least k their minimum bounds the k-th largest from below; otherwise the
+// row minimum does.
+template <int T>
+__device__ __forceinline__ void split_range(const uint32_t* part, int32_t G, int32_t k,
+                                            uint32_t* red, uint32_t& lo, uint32_t& hi) {
+  constexpr int W = T / 64;
+  uint32_t a = 0, bm = 0xFFFFFFFFu, c = 0, d = 0xFFFFFFFFu;
+  for (int g = threadIdx.x; g < G; g += T) {
+    const uint4 q = reinterpret_cast<const uint4*>(part)[g];
+    a = max(a, q.x);
+    bm = min(bm, q.y);
+    c += q.z;
+    d = min(d, q.w);
+  }
+  a = wave_reduce(a, OpMax());
+  bm = wave_reduce(bm, OpMin());
+  c = wave_reduce(c, OpAdd());
+  d = wave_reduce(d, OpMin());
+  const int wid = threadIdx.x >> 6;
+  if (__lane_id() == 0) {
+    red[wid] = a;
+    red[16 + wid] = bm;
+    red[32 + wid] = c;
+    red[48 + wid] = d;
+  }
+  __syncthreads();
+  a = 0, bm = 0xFFFFFFFFu, c = 0, d = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    a = max(a, red[i]);
+    bm = min(bm, red[16 + i]);
+    c += red[32 + i];
+    d = min(d, red[48 + i]);
+  }
+  hi = a;
+  lo = c >= static_cast<uint32_t>(k) ? bm : d;
+}
+
+template <int T, int VEC, int MODE, bool V4>
+__global__ __launch_bounds__(T) void split_hist(Params p, uint32_t* ws, int32_t B, int32_t G,
+                                                int32_t chunk) {
+  __shared__ __align__(16) uint32_t hist[kHistBins + 64];
+  __shared__ uint32_t red[4 * 16];
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const RowRef<MODE> r(p, b);
+  if (r.n <= p.k) return;
+  const SplitWs w(ws, B, G);
+  const Span<T, VEC, V4> span{r.row, g * chunk, chunk_end(g, G, chunk, r.n)};
+  uint32_t key[4 * VEC];
+  hist_clear<T>(hist);
+  uint32_t lo, hi;
+  split_range<T>(w.part + static_cast<int64_t>(b) * G * 4, G, p.k, red, lo, hi);
+  const uint32_t span_k = hi - lo;
+  const int bl = span_k ? 32 - __clz(static_cast<int>(span_k)) : 0;
+  const int s = bl > kHistBits ? bl - kHistBits : 0;
+  uint32_t* rec = w.rec + static_cast<int64_t>(b) * kRec;
+  if (g == 0 && threadIdx.x == 0) {
+    rec[kRecLo] = lo;
+    rec[kRecHi] = hi;
+    rec[kRecShift] = static_cast<uint32_t>(s);
+  }
+  if (span.start >= span.end) return;
+  with_span(span, key, [&](auto res) {
+    constexpr bool RES = decltype(res)::value;
+    bool peel = false;
+    if (RES) {
+      const uint32_t d = key[0] - lo;
+      const uint32_t bin = d >> s;
+      const uint32_t lead = readfirstlane(bin);
+      peel = __popcll(__ballot(d <= span_k && bin == lead)) > kPeelShare;
+    }
+    if (peel) {
+      span.template for_each<RES>(key, [&](uint32_t x, int32_t, int) {
+        const uint32_t d = x - lo;
+        hist_add_peel(hist, d <= span_k, d >> s);
+      });
+    } else {
+      const uint32_t dummy = kHistBins + __lane_id();
+      span.template for_each<RES>(key, [&](uint32_t x, int32_t, int) {
+        const uint32_t d = x - lo;
+        atomicAdd(&hist[d <= span_k ? d >> s : dummy], 1u);
+      });
+    }
+  });
+  __syncthreads();
+  if (lo == 0 && threadIdx.x == 0) hist[0] -= span.pad_slots();
+  __syncthreads();
+  uint32_t* ghist = w.hist + static_cast<int64_t>(b) * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += T) {
+    const uint32_t c = hist[i];
+    if (c) __hip_atomic_fetch_add(&ghist[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+struct alignas(16) SelectSmem {
+  SelSmem sel;
+};
+
+// Per row: threshold bin of the merged histogram; a bucket still above
+// kSmallCap is refined by this workgroup streaming the whole row.
+template <int T, int VEC, int MODE, bool V4>
+__global__ __launch_bounds__(T) void split_select(Params p, uint32_t* ws, int32_t B, int32_t G) {
+  __shared__ SelectSmem sm;
+  const int b = blockIdx.x;
+  const RowRef<MODE> r(p, b);
+  if (r.n <= p.k) return;
+  const SplitWs w(ws, B, G);
+  uint32_t* rec = w.rec + static_cast<int64_t>(b) * kRec;
+  const uint32_t lo = rec[kRecLo], hi = rec[kRecHi];
+  const int s = static_cast<int>(rec[kRecShift]);
+  const uint32_t* ghist = w.hist + static_cast<int64_t>(b) * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins / 4; i += T) {
+    reinterpret_cast<uint4*>(sm.sel.hist[0])[i] = reinterpret_cast<const uint4*>(ghist)[i];
+  }
+  hist_clear<T>(sm.sel.hist[1]);
+  __syncthreads();
+  find_threshold_bin<T>(sm.sel.hist[0], static_cast<uint32_t>(p.k), 0u, sm.sel.wsum, sm.sel.res);
+  Sel sel{};
+  sel.kk = static_cast<uint32_t>(p.k) - sm.sel.res[1];
+  sel.bucket = sm.sel.res[2];
+  sel.lo = lo + (sm.sel.res[0] << s);
+  sel.hi = hi;
+  sel.dhi = static_cast<uint32_t>(r.n - 1);
+  const uint32_t width = (1u << s) - 1u;
+  if (sel.hi - sel.lo > width) sel.hi = sel.lo + width;
+  if (sel.bucket > static_cast<uint32_t>(kSmallCap)) {
+    const Span<T, VEC, V4> span{r.row, 0, r.n};
+    uint32_t key[4 * VEC];
+    int round = 1;
+    sel = refine<T>([&](auto&& f) { span.template for_each<false>(key, f); }, sm.sel, sel,
+                    static_cast<uint32_t>(r.n - 1), span.pad_slots(), 0u, round);
+  }
+  if (threadIdx.x == 0) {
+    rec[kRecLo] = sel.lo;
+    rec[kRecHi] = sel.hi;
+    rec[kRecKk] = sel.kk;
+    rec[kRecTie] = sel.tie;
+    rec[kRecDlo] = sel.dlo;
+    rec[kRecDhi] = sel.dhi;
+  }
+}
+
+template <int T, int VEC, int MODE, bool V4>
+__global__ __launch_bounds__(T) void split_scatter(Params p, uint32_t* ws, int32_t B, int32_t G,
+                                                   int32_t chunk) {
+  constexpr int W = T / 64;
+  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t base[2];
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const RowRef<MODE> r(p, b);
+  if (r.n <= p.k) return;
+  const SplitWs w(ws, B, G);
+  uint32_t* rec = w.rec + static_cast<int64_t>(b) * kRec;
+  const Span<T, VEC, V4> span{r.row, g * chunk, chunk_end(g, G, chunk, r.n)};
+  uint32_t key[4 * VEC];
+  if (span.start >= span.end) return;
+  Sel sel{};
+  sel.lo = rec[kRecLo];
+  sel.hi = rec[kRecHi];
+  sel.kk = rec[kRecKk];
+  sel.tie = rec[kRecTie];
+  sel.dlo = rec[kRecDlo];
+  sel.dhi = rec[kRecDhi];
+  const uint32_t nm1 = static_cast<uint32_t>(r.n - 1);
+  const uint32_t first = static_cast<uint32_t>(p.k) - sel.kk;
+  uint2* cand = w.cand + static_cast<int64_t>(b) * kSmallCap;
+  with_span(span, key, [&](auto res) {
+    constexpr bool RES = decltype(res)::value;
+    uint32_t nw = 0, nc = 0;
+    span.template for_each<RES>(key, [&](uint32_t x, int32_t pos, int) {
+      nw += sel_winner(sel, nm1, span.end, x, pos) ? 1u : 0u;
+      nc += sel_bucket(sel, nm1, span.end, x, pos) ? 1u : 0u;
+    });
+    // one scan of (winners | bucket << 16): a chunk has fewer than 2^16 of each
+    const uint32_t packed = nw | (nc << 16);
+    const uint32_t incl = wave_incl_scan(packed);
+    const int wid = threadIdx.x >> 6;
+    if (__lane_id() == 63) wsum[wid] = incl;
+    __syncthreads();
+    uint32_t off = incl - packed, tot = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      off += (i < wid) ? wsum[i] : 0u;
+      tot += wsum[i];
+    }
+    if (threadIdx.x == 0) {
+      const uint64_t add = (static_cast<uint64_t>(tot & 0xFFFFu) << 32) | (tot >> 16);
+      const uint64_t old = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(rec + kRecCursor), add,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      base[0] = static_cast<uint32_t>(old >> 32);
+      base[1] = static_cast<uint32_t>(old);
+    }
+    __syncthreads();
+    uint32_t wo = base[0] + (off & 0xFFFFu);
+    uint32_t co = base[1] + (off >> 16);
+    span.template for_each<RES>(key, [&](uint32_t x, int32_t pos, int) {
+      if (sel_winner(sel, nm1, span.end, x, pos)) {
+        if (wo < first) r.out[wo] = out_value<MODE>(p, nullptr, r.pt_row, r.row_start, pos);
+        ++wo;
+      }
+      if (sel_bucket(sel, nm1, span.end, x, pos)) {
+        if (co < static_cast<uint32_t>(kSmallCap)) cand[co] = make_uint2(x, static_cast<uint32_t>(pos));
+        ++co;
+      }
+    });
+  });
+}
+
+template <int T, int MODE>
+__global__ __launch_bounds__(T) void split_finish(Params p, uint32_t* ws, int32_t B, int32_t G) {
+  __shared__ uint2 cand[kSmallCap];
+  const int b = blockIdx.x;
+  const RowRef<MODE> r(p, b);
+  if (r.n <= p.k) {
+    emit_whole_row<T, MODE>(p, r);
+    return;
+  }
+  const SplitWs w(ws, B, G);
+  const uint32_t* rec = w.rec + static_cast<int64_t>(b) * kRec;
+  const uint32_t kk = rec[kRecKk];
+  const uint32_t nc = min(rec[kRecCursor], static_cast<uint32_t>(kSmallCap));
+  const uint2* gc = w.cand + static_cast<int64_t>(b) * kSmallCap;
+  for (uint32_t i = threadIdx.x; i < nc; i += T) cand[i] = gc[i];
+  __syncthreads();
+  rank_bucket<T>(cand, nc, kk, static_cast<uint32_t>(p.k) - kk, [&](uint32_t slot, int32_t pos) {
+    r.out[slot] = out_value<MODE>(p, nullptr, r.pt_row, r.row_start, pos);
+  });
 }
 
 }  // namespace ets
@@ -709,22 +1066,97 @@ int32_t page_shift_of(int32_t ps) {
 
 constexpr int kRowThreads = 1024;
 constexpr int kRowVec = 8;  // 8 x float4 per lane -> 32768 scores per tile
-
 constexpr int64_t kRowTile = static_cast<int64_t>(kRowThreads) * 4 * kRowVec;
 
-template <int MODE, bool V4>
-ets_status launch_rows(const ets::Params& p, int32_t B, int64_t max_len, hipStream_t stream) {
-  if (max_len > kRowTile) {
-    hipLaunchKernelGGL((ets::row_topk_kernel<kRowThreads, kRowVec, MODE, V4, true>), dim3(B),
-                       dim3(kRowThreads), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((ets::row_topk_kernel<kRowThreads, kRowVec, MODE, V4, false>), dim3(B),
-                       dim3(kRowThreads), 0, stream, p);
-  }
-  return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
-}
+// row-split path: chunk workgroups of 256 lanes x 16 scores, per-row kernels of 1024 lanes
+constexpr int kSplitThreads = 256;
+constexpr int kSplitVec = 4;
+constexpr int64_t kSplitChunk = static_cast<int64_t>(kSplitThreads) * 4 * kSplitVec;  // 4096
+constexpr int kSelThreads = 1024;
+constexpr int kSelVec = 8;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Chunks per row (0 = one workgroup per row).  A row that fits one resident
+// tile stays on one workgroup; longer rows are cut into kSplitChunk chunks.
+// ETS_ROW_SPLIT = 0 disables splitting; a positive value forces that many
+// chunks per row.
+int32_t split_plan(int32_t B, int64_t max_len) {
+  (void)B;
+  if (const char* e = std::getenv("ETS_ROW_SPLIT"); e != nullptr && *e != '\0') {
+    char* end = nullptr;
+    const long v = std::strtol(e, &end, 10);
+    if (end != e && *end == '\0' && v >= 0 && v <= 65536) {
+      if (v == 0 || max_len <= 0) return 0;
+      return static_cast<int32_t>(std::min<int64_t>(v, (max_len + 3) / 4));
+    }
+  }
+  if (max_len <= kRowTile) return 0;
+  return static_cast<int32_t>((max_len + kSplitChunk - 1) / kSplitChunk);
+}
+
+int32_t split_chunk(int64_t max_len, int32_t G) {
+  const int64_t c = (max_len + G - 1) / G;
+  return static_cast<int32_t>((c + 3) / 4 * 4);
+}
+
+size_t split_ws_bytes(int32_t B, int32_t G) {
+  const size_t words = static_cast<size_t>(B) *
+                       (ets::kRec + 4 * static_cast<size_t>(G) + ets::kHistBins + 2 * ets::kSmallCap);
+  return (words * 4 + 255) / 256 * 256;
+}
+
+// Host-side check of the split path's workspace, before any HIP call.
+ets_status check_workspace(int32_t B, int64_t max_len, const void* ws, size_t ws_bytes) {
+  const int32_t G = split_plan(B, max_len);
+  if (G == 0) return ETS_OK;
+  if (static_cast<int64_t>(B) * G > INT32_MAX) return ETS_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < split_ws_bytes(B, G) || !aligned16(ws)) return ETS_ERR_WORKSPACE;
+  return ETS_OK;
+}
+
+template <int MODE, bool V4, int VEC, bool STREAM>
+void launch_rows(const ets::Params& p, int32_t B, hipStream_t stream) {
+  hipLaunchKernelGGL((ets::row_topk_kernel<kRowThreads, VEC, MODE, V4, STREAM>), dim3(B),
+                     dim3(kRowThreads), 0, stream, p);
+}
+
+template <int MODE, bool V4>
+ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+  const int32_t G = split_plan(B, max_len);
+  if (G == 0) {
+    // the smallest resident tile (1024 lanes x 4 VEC scores) that holds the row
+    if (max_len <= kRowTile / 4) {
+      launch_rows<MODE, V4, kRowVec / 4, false>(p, B, stream);
+    } else if (max_len <= kRowTile / 2) {
+      launch_rows<MODE, V4, kRowVec / 2, false>(p, B, stream);
+    } else if (max_len <= kRowTile) {
+      launch_rows<MODE, V4, kRowVec, false>(p, B, stream);
+    } else {
+      launch_rows<MODE, V4, kRowVec, true>(p, B, stream);
+    }
+    return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
+  }
+  // (workspace already validated by check_workspace)
+  const int32_t chunk = split_chunk(max_len, G);
+  auto* w = static_cast<uint32_t*>(ws);
+  const int64_t zero_words = static_cast<int64_t>(B) * (ets::kRec + ets::kHistBins);
+  const int zero_blocks = static_cast<int>(std::min<int64_t>(1024, (zero_words + 255) / 256));
+  const dim3 chunks(static_cast<uint32_t>(B) * G), rows(B);
+  hipLaunchKernelGGL(ets::split_zero, dim3(zero_blocks), dim3(256), 0, stream, w, B, G);
+  hipLaunchKernelGGL((ets::split_bounds<kSplitThreads, kSplitVec, MODE, V4>), chunks,
+                     dim3(kSplitThreads), 0, stream, p, w, B, G, chunk);
+  hipLaunchKernelGGL((ets::split_hist<kSplitThreads, kSplitVec, MODE, V4>), chunks,
+                     dim3(kSplitThreads), 0, stream, p, w, B, G, chunk);
+  hipLaunchKernelGGL((ets::split_select<kSelThreads, kSelVec, MODE, V4>), rows, dim3(kSelThreads),
+                     0, stream, p, w, B, G);
+  hipLaunchKernelGGL((ets::split_scatter<kSplitThreads, kSplitVec, MODE, V4>), chunks,
+                     dim3(kSplitThreads), 0, stream, p, w, B, G, chunk);
+  hipLaunchKernelGGL((ets::split_finish<kSelThreads, MODE>), rows, dim3(kSelThreads), 0, stream, p,
+                     w, B, G);
+  return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
+}
 
 }  // namespace
 
@@ -743,15 +1175,8 @@ const char* ets_status_string(ets_status status) {
 }
 
 int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count) {
-  if (const char* e = std::getenv("ETS_ROW_SPLIT"); e != nullptr && *e != '\0') {
-    char* end = nullptr;
-    const long v = std::strtol(e, &end, 10);
-    if (end != e && *end == '\0' && v >= 0 && v <= 1024) return static_cast<int32_t>(v);
-  }
-  (void)B;
-  (void)max_row_len;
   (void)cu_count;
-  return 0;
+  return split_plan(B, max_row_len);
 }
 
 ets_status ets_workspace_size(int32_t B, int64_t max_row_len, int32_t k, int32_t device,
@@ -759,19 +1184,19 @@ ets_status ets_workspace_size(int32_t B, int64_t max_row_len, int32_t k, int32_t
   if (!bytes || B < 0 || max_row_len < 0) return ETS_ERR_INVALID_ARG;
   if (k < 1 || k > ETS_MAX_K) return ETS_ERR_K_RANGE;
   (void)device;
-  *bytes = 0;
+  const int32_t G = split_plan(B, max_row_len);
+  *bytes = (G == 0 || B == 0) ? 0 : split_ws_bytes(B, G);
   return ETS_OK;
 }
 
 ets_status ets_topk_raw(const float* scores, int64_t row_stride, int32_t B, int32_t L,
                         const int32_t* lens, int32_t k, int32_t* out, int64_t out_stride,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (k < 1 || k > ETS_MAX_K) return ETS_ERR_K_RANGE;
   if (B < 0 || L < 0 || row_stride < L || out_stride < k) return ETS_ERR_INVALID_ARG;
   if (B == 0) return ETS_OK;
   if (!out || (L > 0 && !scores)) return ETS_ERR_INVALID_ARG;
+  if (ets_status st = check_workspace(B, L, workspace, workspace_bytes); st != ETS_OK) return st;
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
@@ -786,20 +1211,20 @@ ets_status ets_topk_raw(const float* scores, int64_t row_stride, int32_t B, int3
   p.page_shift = -1;
   const bool v4 = aligned16(scores) && (row_stride % 4 == 0) && (L % 4 == 0);
   auto s = static_cast<hipStream_t>(stream);
-  return v4 ? launch_rows<ets::kRaw, true>(p, B, L, s) : launch_rows<ets::kRaw, false>(p, B, L, s);
+  return v4 ? launch<ets::kRaw, true>(p, B, L, workspace, workspace_bytes, s)
+            : launch<ets::kRaw, false>(p, B, L, workspace, workspace_bytes, s);
 }
 
 ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, int32_t L,
                           const int32_t* seq_lens, const int32_t* page_table, int64_t pt_stride,
                           int32_t page_size, int32_t k, int32_t* out, int64_t out_stride,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (k < 1 || k > ETS_MAX_K) return ETS_ERR_K_RANGE;
   if (B < 0 || L < 0 || row_stride < L || out_stride < k || page_size < 1 || pt_stride < 0)
     return ETS_ERR_INVALID_ARG;
   if (B == 0) return ETS_OK;
   if (!out || !seq_lens || !page_table || (L > 0 && !scores)) return ETS_ERR_INVALID_ARG;
+  if (ets_status st = check_workspace(B, L, workspace, workspace_bytes); st != ETS_OK) return st;
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
@@ -817,19 +1242,20 @@ ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, in
   p.out_stride = out_stride;
   const bool v4 = aligned16(scores) && (row_stride % 4 == 0) && (L % 4 == 0);
   auto s = static_cast<hipStream_t>(stream);
-  return v4 ? launch_rows<ets::kPaged, true>(p, B, L, s) : launch_rows<ets::kPaged, false>(p, B, L, s);
+  return v4 ? launch<ets::kPaged, true>(p, B, L, workspace, workspace_bytes, s)
+            : launch<ets::kPaged, false>(p, B, L, workspace, workspace_bytes, s);
 }
 
 ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,
                            const int32_t* lengths, int32_t B, int64_t max_len_hint, int32_t k,
                            int32_t* out, int64_t out_stride, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (k < 1 || k > ETS_MAX_K) return ETS_ERR_K_RANGE;
   if (B < 0 || max_len_hint < 0 || out_stride < k) return ETS_ERR_INVALID_ARG;
   if (B == 0) return ETS_OK;
   if (!out || !row_starts || !lengths || !packed) return ETS_ERR_INVALID_ARG;
+  if (ets_status st = check_workspace(B, max_len_hint, workspace, workspace_bytes); st != ETS_OK)
+    return st;
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
@@ -841,7 +1267,8 @@ ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,
   p.out = out;
   p.out_stride = out_stride;
   p.page_shift = -1;
-  return launch_rows<ets::kRagged, false>(p, B, max_len_hint, static_cast<hipStream_t>(stream));
+  return launch<ets::kRagged, false>(p, B, max_len_hint, workspace, workspace_bytes,
+                                     static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -95,3 +95,38 @@ def test_row_split_env_override(tmp_path):
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                          check=True).stdout.split()
     assert out == ["0", "0"]
+
+
+def test_row_split_heuristic_and_workspace(lib):
+    import exact_top_selection_amd as ets
+    env = os.environ.pop("ETS_ROW_SPLIT", None)
+    try:
+        # rows that fit one resident workgroup tile stay whole
+        assert ets.row_split(64, 32768, 256) == 0
+        assert ets.row_split(1, 2048, 256) == 0
+        # longer rows are cut into 4096-score chunks
+        assert ets.row_split(4, 32769, 256) == 9
+        assert ets.row_split(4, 262144, 256) == 64
+        assert ets.workspace_size(64, 32768, 1024) == 0
+        n = ets.workspace_size(4, 262144, 2048)
+        words = 4 * (16 + 4 * 64 + 4096 + 2 * 128)
+        assert n == (words * 4 + 255) // 256 * 256
+    finally:
+        if env is not None:
+            os.environ["ETS_ROW_SPLIT"] = env
+
+
+def test_split_call_rejects_small_workspace(lib):
+    import ctypes as C
+    env = os.environ.get("ETS_ROW_SPLIT")
+    os.environ["ETS_ROW_SPLIT"] = "4"
+    try:
+        fake = C.c_void_p(0x1000)
+        # a split call without its workspace is rejected before any HIP call
+        st = lib.ets_topk_raw(fake, 65536, 2, 65536, None, 8, fake, 8, None, 0, None)
+        assert st == 3
+    finally:
+        if env is None:
+            os.environ.pop("ETS_ROW_SPLIT", None)
+        else:
+            os.environ["ETS_ROW_SPLIT"] = env
