@@ -216,30 +216,62 @@ struct Span {
     const int32_t last = len - ((len - 1) / TILE) * TILE;
     return static_cast<uint32_t>(TILE - last);
   }
+  // Loads the tile at base.  Every lane issues all of its loads before any
+  // key is formed, so the loads overlap; lanes past the end re-read the last
+  // in-range word (V4: float4), which keeps each access inside the row (V4
+  // rows have a capacity that is a multiple of 4).  Slot groups that lie
+  // wholly inside, straddle or lie past the end are told apart per group, the
+  // same for all lanes.
   __device__ __forceinline__ void load(Keys& key, int32_t base) const {
     const int32_t tid = static_cast<int32_t>(threadIdx.x);
+    if (base >= end) {
+#pragma unroll
+      for (int j = 0; j < PT; ++j) key[j] = 0u;
+      return;
+    }
     if constexpr (V4) {
+      const int32_t qlast = (end - 1) & ~3;
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
-        const int32_t q = base + 4 * (v * T + tid);
-        if (q + 3 < end) {
-          const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + q));
-          key[4 * v + 0] = order_key(w.x);
-          key[4 * v + 1] = order_key(w.y);
-          key[4 * v + 2] = order_key(w.z);
-          key[4 * v + 3] = order_key(w.w);
-        } else {
+        const int32_t q = min(base + 4 * (v * T + tid), qlast);
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + q));
+        key[4 * v + 0] = w.x;
+        key[4 * v + 1] = w.y;
+        key[4 * v + 2] = w.z;
+        key[4 * v + 3] = w.w;
+      }
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            key[4 * v + c] = (q + c < end) ? order_key(__float_as_uint(row[q + c])) : 0u;
+      for (int v = 0; v < VEC; ++v) {
+        const int32_t g0 = base + 4 * v * T;  // first position of the group
+        const int32_t q = g0 + 4 * tid;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint32_t& x = key[4 * v + c];
+          if (g0 + 4 * T <= end) {
+            x = order_key(x);
+          } else if (g0 >= end) {
+            x = 0u;
+          } else {
+            x = q + c < end ? order_key(x) : 0u;
           }
         }
       }
     } else {
 #pragma unroll
       for (int j = 0; j < PT; ++j) {
-        const int32_t q = base + j * T + tid;
-        key[j] = (q < end) ? order_key(__builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row) + q)) : 0u;
+        const int32_t q = min(base + j * T + tid, end - 1);
+        key[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row) + q);
+      }
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const int32_t g0 = base + j * T;
+        if (g0 + T <= end) {
+          key[j] = order_key(key[j]);
+        } else if (g0 >= end) {
+          key[j] = 0u;
+        } else {
+          key[j] = g0 + tid < end ? order_key(key[j]) : 0u;
+        }
       }
     }
   }
@@ -385,9 +417,15 @@ __device__ __forceinline__ bool sel_bucket(const Sel& s, uint32_t nm1, int32_t e
          (s.hi != 0 || pos < end);
 }
 
-// Output value of selected position pos of a row.
+// Address-space qualified views: a read through them compiles to an LDS or a
+// global load, never to a flat one.
+using lds_i32 = __attribute__((address_space(3))) const int32_t;
+using glb_i32 = __attribute__((address_space(1))) const int32_t;
+
+// Output value of selected position pos of a row.  Paged: pt_lds is the
+// row's page-table staged in LDS, used when use_lds, else pt_row is read.
 template <int MODE>
-__device__ __forceinline__ int32_t out_value(const Params& p, const int32_t* pt_lds,
+__device__ __forceinline__ int32_t out_value(const Params& p, bool use_lds, const int32_t* pt_lds,
                                              const int32_t* pt_row, int32_t row_start, int32_t pos) {
   if constexpr (MODE == kPaged) {
     int32_t page, off;
@@ -398,7 +436,8 @@ __device__ __forceinline__ int32_t out_value(const Params& p, const int32_t* pt_
       page = pos / p.page_size;
       off = pos - page * p.page_size;
     }
-    return (pt_lds ? pt_lds[page] : pt_row[page]) * p.page_size + off;
+    const int32_t id = use_lds ? ((lds_i32*)pt_lds)[page] : ((glb_i32*)pt_row)[page];
+    return id * p.page_size + off;
   } else if constexpr (MODE == kRagged) {
     return row_start + pos;
   } else {
@@ -409,23 +448,25 @@ __device__ __forceinline__ int32_t out_value(const Params& p, const int32_t* pt_
 // Ranks up to kSmallCap bucket entries on (key desc, position asc) and emits
 // the kk best at slots first + rank.  Eight lanes share an entry: each
 // compares it with every eighth entry, then row permutes sum the counts.
+// (key, ~position) as one 64-bit word orders the entries the same way.
 template <int T, class Emit>
 __device__ __forceinline__ void rank_bucket(const uint2* cand, uint32_t nc, uint32_t kk,
                                             uint32_t first, Emit&& emit) {
   static_assert(T >= 8 * kSmallCap, "eight lanes per bucket entry");
+  constexpr int Q = kSmallCap / 8;
   const uint32_t i = threadIdx.x >> 3;
   const uint32_t part = threadIdx.x & 7;
-  uint32_t rank = 0;
-  uint2 ci = make_uint2(0, 0);
-  if (i < nc) {
-    ci = cand[i];
+  const uint32_t last = nc > 0 ? nc - 1 : 0;
+  const uint2 ci = cand[min(i, last)];
+  uint2 cj[Q];
 #pragma unroll
-    for (uint32_t q = 0; q < kSmallCap / 8; ++q) {
-      const uint32_t j = part + 8 * q;
-      const uint2 cj = cand[min(j, nc - 1)];
-      const bool before = cj.x > ci.x || (cj.x == ci.x && static_cast<int32_t>(cj.y) < static_cast<int32_t>(ci.y));
-      rank += (j < nc && before) ? 1u : 0u;
-    }
+  for (int q = 0; q < Q; ++q) cj[q] = cand[min(part + 8 * q, last)];
+  const uint64_t vi = (static_cast<uint64_t>(ci.x) << 32) | static_cast<uint32_t>(~ci.y);
+  uint32_t rank = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint64_t vj = (static_cast<uint64_t>(cj[q].x) << 32) | static_cast<uint32_t>(~cj[q].y);
+    rank += static_cast<uint32_t>((part + 8 * q < nc) & (vj > vi));
   }
   rank += dpp_perm<0xB1>(rank);   // quad_perm [1,0,3,2]
   rank += dpp_perm<0x4E>(rank);   // quad_perm [2,3,0,1]
@@ -460,7 +501,7 @@ struct RowRef {
 template <int T, int MODE>
 __device__ __forceinline__ void emit_whole_row(const Params& p, const RowRef<MODE>& r) {
   for (int32_t i = threadIdx.x; i < p.k; i += T) {
-    r.out[i] = (i < r.n) ? out_value<MODE>(p, nullptr, r.pt_row, r.row_start, i) : -1;
+    r.out[i] = (i < r.n) ? out_value<MODE>(p, false, nullptr, r.pt_row, r.row_start, i) : -1;
   }
 }
 
@@ -579,9 +620,19 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
   // ---- scatter: append the bucket to LDS, count the winners, place them by
   // one block scan (whose barrier also publishes the bucket), emit them.
   const uint32_t first = static_cast<uint32_t>(k) - sel.kk;  // number of winners
-  const int32_t* pt_stage = pt_lds ? sm.pt : nullptr;
-  auto emit = [&](uint32_t slot, int32_t pos) {
-    r.out[slot] = out_value<MODE>(p, pt_stage, r.pt_row, r.row_start, pos);
+  // the page-table source is chosen once per row, so that each emitting loop
+  // reads only LDS (or only global memory) and never waits on its stores
+  auto emitter = [&](auto lds) {
+    return [&](uint32_t slot, int32_t pos) {
+      r.out[slot] = out_value<MODE>(p, decltype(lds)::value, sm.pt, r.pt_row, r.row_start, pos);
+    };
+  };
+  auto with_emit = [&](auto&& body) {
+    if (MODE != kPaged || pt_lds) {
+      body(emitter(std::true_type()));
+    } else {
+      body(emitter(std::false_type()));
+    }
   };
   auto append = [&](uint32_t x, int32_t pos) {
     const uint32_t slot = atomicAdd(&sm.ccount, 1u);
@@ -616,12 +667,14 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
 #pragma unroll
     for (int w = 0; w < W; ++w) off += (w < wid) ? sm.sel.wsum[w] : 0u;
     // the bound only guards the row against a broken invariant
-    while (wmask != 0) {
-      const int j = __ffs(static_cast<int>(wmask)) - 1;
-      wmask &= wmask - 1u;
-      if (off < first) emit(off, tile_pos<T, V4>(j));
-      ++off;
-    }
+    with_emit([&](auto emit) {
+      while (wmask != 0) {
+        const int j = __ffs(static_cast<int>(wmask)) - 1;
+        wmask &= wmask - 1u;
+        if (off < first) emit(off, tile_pos<T, V4>(j));
+        ++off;
+      }
+    });
   } else {
     uint32_t nwin = 0;
     for_each([&](uint32_t x, int32_t pos, int) {
@@ -635,16 +688,20 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
     uint32_t off = incl - nwin;
 #pragma unroll
     for (int w = 0; w < W; ++w) off += (w < wid) ? sm.sel.wsum[w] : 0u;
-    for_each([&](uint32_t x, int32_t pos, int) {
-      if (sel_winner(sel, nm1, span.end, x, pos)) {
-        if (off < first) emit(off, pos);
-        ++off;
-      }
+    with_emit([&](auto emit) {
+      for_each([&](uint32_t x, int32_t pos, int) {
+        if (sel_winner(sel, nm1, span.end, x, pos)) {
+          if (off < first) emit(off, pos);
+          ++off;
+        }
+      });
     });
   }
 
   // ---- the bucket's best kk, placed by rank
-  rank_bucket<T>(sm.cand, min(sm.ccount, static_cast<uint32_t>(kSmallCap)), sel.kk, first, emit);
+  with_emit([&](auto emit) {
+    rank_bucket<T>(sm.cand, min(sm.ccount, static_cast<uint32_t>(kSmallCap)), sel.kk, first, emit);
+  });
 }
 
 // One workgroup per row.  STREAM = false: rows fit one tile (the host
@@ -991,7 +1048,7 @@ __global__ __launch_bounds__(T) void split_scatter(Params p, uint32_t* ws, int32
     uint32_t co = base[1] + (off >> 16);
     span.template for_each<RES>(key, [&](uint32_t x, int32_t pos, int) {
       if (sel_winner(sel, nm1, span.end, x, pos)) {
-        if (wo < first) r.out[wo] = out_value<MODE>(p, nullptr, r.pt_row, r.row_start, pos);
+        if (wo < first) r.out[wo] = out_value<MODE>(p, false, nullptr, r.pt_row, r.row_start, pos);
         ++wo;
       }
       if (sel_bucket(sel, nm1, span.end, x, pos)) {
@@ -1019,7 +1076,7 @@ __global__ __launch_bounds__(T) void split_finish(Params p, uint32_t* ws, int32_
   for (uint32_t i = threadIdx.x; i < nc; i += T) cand[i] = gc[i];
   __syncthreads();
   rank_bucket<T>(cand, nc, kk, static_cast<uint32_t>(p.k) - kk, [&](uint32_t slot, int32_t pos) {
-    r.out[slot] = out_value<MODE>(p, nullptr, r.pt_row, r.row_start, pos);
+    r.out[slot] = out_value<MODE>(p, false, nullptr, r.pt_row, r.row_start, pos);
   });
 }
 
