@@ -113,6 +113,18 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
   return op(op(readlane(x, 0), readlane(x, 16)), op(readlane(x, 32), readlane(x, 48)));
 }
 
+// Sum of the per-wave totals wsum[w] over the waves below (BELOW) or above
+// the calling wave: one LDS read per lane and a wave reduction, uniform.
+template <int W, bool BELOW>
+__device__ __forceinline__ uint32_t sum_other_waves(const uint32_t* wsum) {
+  static_assert(W <= 64, "one lane per wave");
+  const int lane = static_cast<int>(__lane_id());
+  const int wid = static_cast<int>(threadIdx.x >> 6);
+  const uint32_t v = wsum[min(lane, W - 1)];
+  const bool take = lane < W && (BELOW ? lane < wid : lane > wid);
+  return wave_reduce(take ? v : 0u, OpAdd());
+}
+
 // Adds one to hist[bin] for every lane with `pred` (call in uniform control
 // flow).  Lanes that share lane 0's bin are merged into one LDS atomic issued
 // by lane 0, which removes the serialisation when most of a wave lands in one
@@ -154,9 +166,8 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, uint32_
   const uint32_t incl = wave_incl_scan(s);
   if (__lane_id() == 63) wsum[wid] = incl;
   __syncthreads();
-  uint32_t above = readlane(incl, 63) - incl;  // higher lanes of this wave
-#pragma unroll
-  for (int w = 0; w < W; ++w) above += (w > wid) ? wsum[w] : 0u;
+  // higher lanes of this wave, then the waves above
+  uint32_t above = readlane(incl, 63) - incl + sum_other_waves<W, false>(wsum);
 #pragma unroll
   for (int i = BPT - 1; i >= 0; --i) {
     if (above < kk && kk <= above + h[i]) {
@@ -511,6 +522,7 @@ struct alignas(16) RowSmem {
   SelSmem sel;
   int32_t pt[kPtCap];     // staged page-table row (paged map)
   uint2 cand[kSmallCap];  // threshold bucket: (key, position)
+  int32_t pos[ETS_MAX_K]; // selected positions by output slot
   uint32_t red[64];       // per-wave partials (bounds)
   uint32_t ccount;
 };
@@ -618,7 +630,8 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
   const Sel sel = refine<T>(for_each, sm.sel, sel0, nm1, span.pad_slots(), key[0], round);
 
   // ---- scatter: append the bucket to LDS, count the winners, place them by
-  // one block scan (whose barrier also publishes the bucket), emit them.
+  // one block scan (whose barrier also publishes the bucket) into the
+  // position list.
   const uint32_t first = static_cast<uint32_t>(k) - sel.kk;  // number of winners
   // the page-table source is chosen once per row, so that each emitting loop
   // reads only LDS (or only global memory) and never waits on its stores
@@ -639,22 +652,31 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
     if (slot < static_cast<uint32_t>(kSmallCap)) sm.cand[slot] = make_uint2(x, static_cast<uint32_t>(pos));
   };
   if constexpr (!STREAM) {
-    uint32_t wmask = 0, cmask = 0;  // bit j: slot j is a winner / in the bucket
+    // bit PT-1-j of wmask / cmask: slot j is a winner / in the bucket
+    static_assert(PT <= 32, "slot masks are 32 bits");
+    uint32_t wmask = 0, cmask = 0;
     if (!sel.tie) {
-      const uint32_t khi = sel.hi;
-      for_each([&](uint32_t x, int32_t pos, int j) {
-        wmask |= (x > khi ? 1u : 0u) << j;
-        cmask |= (sel_bucket(sel, nm1, n, x, pos) ? 1u : 0u) << j;
-      });
+      const uint32_t khi = sel.hi, klo = sel.lo, kspan = sel.hi - sel.lo;
+      if (klo != 0) {
+        for_each([&](uint32_t x, int32_t, int) {
+          wmask = wmask + wmask + (x > khi ? 1u : 0u);
+          cmask = cmask + cmask + (x - klo <= kspan ? 1u : 0u);
+        });
+      } else {
+        for_each([&](uint32_t x, int32_t pos, int) {
+          wmask = wmask + wmask + (x > khi ? 1u : 0u);
+          cmask = cmask + cmask + (x - klo <= kspan && pos < n ? 1u : 0u);
+        });
+      }
     } else {
-      for_each([&](uint32_t x, int32_t pos, int j) {
-        wmask |= (sel_winner(sel, nm1, span.end, x, pos) ? 1u : 0u) << j;
-        cmask |= (sel_bucket(sel, nm1, n, x, pos) ? 1u : 0u) << j;
+      for_each([&](uint32_t x, int32_t pos, int) {
+        wmask = wmask + wmask + (sel_winner(sel, nm1, span.end, x, pos) ? 1u : 0u);
+        cmask = cmask + cmask + (sel_bucket(sel, nm1, n, x, pos) ? 1u : 0u);
       });
     }
     if (__ballot(cmask != 0) != 0) {
       while (cmask != 0) {
-        const int j = __ffs(static_cast<int>(cmask)) - 1;
+        const int j = PT - __ffs(static_cast<int>(cmask));
         cmask &= cmask - 1u;
         append(select_slot<PT>(key, j), tile_pos<T, V4>(j));
       }
@@ -663,18 +685,14 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
     const uint32_t incl = wave_incl_scan(nwin);
     if (__lane_id() == 63) sm.sel.wsum[wid] = incl;
     __syncthreads();
-    uint32_t off = incl - nwin;
-#pragma unroll
-    for (int w = 0; w < W; ++w) off += (w < wid) ? sm.sel.wsum[w] : 0u;
+    uint32_t off = incl - nwin + sum_other_waves<W, true>(sm.sel.wsum);
     // the bound only guards the row against a broken invariant
-    with_emit([&](auto emit) {
-      while (wmask != 0) {
-        const int j = __ffs(static_cast<int>(wmask)) - 1;
-        wmask &= wmask - 1u;
-        if (off < first) emit(off, tile_pos<T, V4>(j));
-        ++off;
-      }
-    });
+    while (wmask != 0) {
+      const int j = PT - __ffs(static_cast<int>(wmask));
+      wmask &= wmask - 1u;
+      if (off < first) sm.pos[off] = tile_pos<T, V4>(j);
+      ++off;
+    }
   } else {
     uint32_t nwin = 0;
     for_each([&](uint32_t x, int32_t pos, int) {
@@ -685,22 +703,23 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
     const uint32_t incl = wave_incl_scan(nwin);
     if (__lane_id() == 63) sm.sel.wsum[wid] = incl;
     __syncthreads();
-    uint32_t off = incl - nwin;
-#pragma unroll
-    for (int w = 0; w < W; ++w) off += (w < wid) ? sm.sel.wsum[w] : 0u;
-    with_emit([&](auto emit) {
-      for_each([&](uint32_t x, int32_t pos, int) {
-        if (sel_winner(sel, nm1, span.end, x, pos)) {
-          if (off < first) emit(off, pos);
-          ++off;
-        }
-      });
+    uint32_t off = incl - nwin + sum_other_waves<W, true>(sm.sel.wsum);
+    for_each([&](uint32_t x, int32_t pos, int) {
+      if (sel_winner(sel, nm1, span.end, x, pos)) {
+        if (off < first) sm.pos[off] = pos;
+        ++off;
+      }
     });
   }
 
   // ---- the bucket's best kk, placed by rank
+  rank_bucket<T>(sm.cand, min(sm.ccount, static_cast<uint32_t>(kSmallCap)), sel.kk, first,
+                 [&](uint32_t slot, int32_t pos) { sm.pos[slot] = pos; });
+  __syncthreads();
+
+  // ---- emit the k selected positions through the output map, coalesced
   with_emit([&](auto emit) {
-    rank_bucket<T>(sm.cand, min(sm.ccount, static_cast<uint32_t>(kSmallCap)), sel.kk, first, emit);
+    for (int32_t i = tid; i < k; i += T) emit(static_cast<uint32_t>(i), sm.pos[i]);
   });
 }
 
