@@ -457,31 +457,37 @@ __device__ __forceinline__ int32_t out_value(const Params& p, bool use_lds, cons
 }
 
 // Ranks up to kSmallCap bucket entries on (key desc, position asc) and emits
-// the kk best at slots first + rank.  Eight lanes share an entry: each
-// compares it with every eighth entry, then row permutes sum the counts.
+// the kk best at slots first + rank.  G = T / kSmallCap lanes share an entry:
+// each compares it with every G-th entry, then row permutes sum the G counts.
 // (key, ~position) as one 64-bit word orders the entries the same way.
 template <int T, class Emit>
 __device__ __forceinline__ void rank_bucket(const uint2* cand, uint32_t nc, uint32_t kk,
                                             uint32_t first, Emit&& emit) {
-  static_assert(T >= 8 * kSmallCap, "eight lanes per bucket entry");
-  constexpr int Q = kSmallCap / 8;
-  const uint32_t i = threadIdx.x >> 3;
-  const uint32_t part = threadIdx.x & 7;
+  constexpr int G = T / kSmallCap;
+  static_assert(G == 2 || G == 4 || G == 8, "2, 4 or 8 lanes per bucket entry");
+  constexpr int Q = kSmallCap / G;  // entries compared by each lane
+  constexpr int QB = 16;            // entries read per batch
+  const uint32_t i = threadIdx.x / G;
+  const uint32_t part = threadIdx.x % G;
   const uint32_t last = nc > 0 ? nc - 1 : 0;
   const uint2 ci = cand[min(i, last)];
-  uint2 cj[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) cj[q] = cand[min(part + 8 * q, last)];
   const uint64_t vi = (static_cast<uint64_t>(ci.x) << 32) | static_cast<uint32_t>(~ci.y);
   uint32_t rank = 0;
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const uint64_t vj = (static_cast<uint64_t>(cj[q].x) << 32) | static_cast<uint32_t>(~cj[q].y);
-    rank += static_cast<uint32_t>((part + 8 * q < nc) & (vj > vi));
+  for (int q0 = 0; q0 < Q; q0 += QB) {
+    if (static_cast<uint32_t>(G * q0) >= nc) break;
+    uint2 cj[QB];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) cj[q] = cand[min(part + G * (q0 + q), last)];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const uint64_t vj = (static_cast<uint64_t>(cj[q].x) << 32) | static_cast<uint32_t>(~cj[q].y);
+      rank += static_cast<uint32_t>((part + G * (q0 + q) < nc) & (vj > vi));
+    }
   }
-  rank += dpp_perm<0xB1>(rank);   // quad_perm [1,0,3,2]
-  rank += dpp_perm<0x4E>(rank);   // quad_perm [2,3,0,1]
-  rank += dpp_perm<0x141>(rank);  // row_half_mirror: the other quad of the eight
+  rank += dpp_perm<0xB1>(rank);                         // quad_perm [1,0,3,2]: pairs
+  if constexpr (G >= 4) rank += dpp_perm<0x4E>(rank);   // quad_perm [2,3,0,1]: quads
+  if constexpr (G >= 8) rank += dpp_perm<0x141>(rank);  // row_half_mirror: eights
   if (i < nc && part == 0 && rank < kk) emit(first + rank, static_cast<int32_t>(ci.y));
 }
 
@@ -1191,10 +1197,10 @@ ets_status check_workspace(int32_t B, int64_t max_len, const void* ws, size_t ws
   return ETS_OK;
 }
 
-template <int MODE, bool V4, int VEC, bool STREAM>
+template <int MODE, bool V4, int T, int VEC, bool STREAM>
 void launch_rows(const ets::Params& p, int32_t B, hipStream_t stream) {
-  hipLaunchKernelGGL((ets::row_topk_kernel<kRowThreads, VEC, MODE, V4, STREAM>), dim3(B),
-                     dim3(kRowThreads), 0, stream, p);
+  hipLaunchKernelGGL((ets::row_topk_kernel<T, VEC, MODE, V4, STREAM>), dim3(B), dim3(T), 0, stream,
+                     p);
 }
 
 template <int MODE, bool V4>
@@ -1203,14 +1209,21 @@ ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, void* ws, si
   const int32_t G = split_plan(B, max_len);
   if (G == 0) {
     // the smallest resident tile (1024 lanes x 4 VEC scores) that holds the row
-    if (max_len <= kRowTile / 4) {
-      launch_rows<MODE, V4, kRowVec / 4, false>(p, B, stream);
+    // the smallest resident tile that holds the row, with as few scores per
+    // lane as the lane count allows: the passes are latency bound, and more
+    // waves with shorter slot loops hide more of it
+    if (max_len <= 2048) {
+      launch_rows<MODE, V4, 512, 1, false>(p, B, stream);
+    } else if (max_len <= 4096) {
+      launch_rows<MODE, V4, kRowThreads, 1, false>(p, B, stream);
+    } else if (max_len <= kRowTile / 4) {
+      launch_rows<MODE, V4, kRowThreads, kRowVec / 4, false>(p, B, stream);
     } else if (max_len <= kRowTile / 2) {
-      launch_rows<MODE, V4, kRowVec / 2, false>(p, B, stream);
+      launch_rows<MODE, V4, kRowThreads, kRowVec / 2, false>(p, B, stream);
     } else if (max_len <= kRowTile) {
-      launch_rows<MODE, V4, kRowVec, false>(p, B, stream);
+      launch_rows<MODE, V4, kRowThreads, kRowVec, false>(p, B, stream);
     } else {
-      launch_rows<MODE, V4, kRowVec, true>(p, B, stream);
+      launch_rows<MODE, V4, kRowThreads, kRowVec, true>(p, B, stream);
     }
     return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
   }

@@ -203,3 +203,42 @@ def test_invalid_arguments_raise():
         ets.topk_raw(s, 4096)
     with pytest.raises(TypeError):
         ets.topk_raw(s.double(), 8)
+
+
+# Row capacities at and around each resident tile size (2048 and 4096 scores
+# on 256 / 512 lanes, 8192 / 16384 / 32768 on 1024 lanes).
+@pytest.mark.parametrize("L", [1100, 2048, 2049, 4096, 4097, 8192, 8193, 16384, 16385, 32768])
+def test_every_tile_size(L):
+    rng = np.random.default_rng(L)
+    print("case tile L", L, flush=True)
+    x = rng.standard_normal((4, L)).astype(np.float32)
+    lens = np.array([L, L - 1, (L + 1) // 2, 1030], dtype=np.int32)
+    for k in (1, 1024):
+        w = _dense("tile", "raw", x, k, lens)
+        assert_parity(w, run_gpu(w), run_oracle(w))
+    pt = np.stack([rng.permutation((L + 63) // 64) for _ in range(4)]).astype(np.int32)
+    w = _dense("tile-paged", "paged", x, 1024, lens, pt=pt)
+    assert_parity(w, run_gpu(w), run_oracle(w))
+    crng = np.random.Generator(np.random.PCG64(L))
+    y = np.stack([workloads.concentrated_row(crng, L) for _ in range(2)])
+    w = _dense("tile-concentrated", "raw", y, min(2048, L - 1))
+    assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+@pytest.mark.parametrize("hint", [1500, 3000, 6000])
+def test_ragged_hint_below_row_length(hint):
+    """Rows longer than the length hint take the streamed passes of the
+    hinted tile size."""
+    rng = np.random.default_rng(hint)
+    lengths = np.array([hint, 3 * hint + 5, 20000, 1025, 0], dtype=np.int32)
+    starts = np.zeros_like(lengths)
+    starts[1:] = np.cumsum(lengths[:-1])
+    packed = rng.standard_normal(int(lengths.sum())).astype(np.float32)
+    d = dev()
+    for k in (1, 1024):
+        w = Workload("ragged-short-hint", "ragged", k, lengths.shape[0], packed,
+                     row_starts=starts, lengths=lengths)
+        out = ets.topk_ragged(torch.from_numpy(packed).to(d), torch.from_numpy(starts).to(d),
+                              torch.from_numpy(lengths).to(d), k, max_len=hint)
+        torch.cuda.synchronize()
+        assert_parity(w, out.cpu().numpy(), run_oracle(w))
