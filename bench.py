@@ -208,23 +208,23 @@ def main() -> int:
     ring.copy_(scores0.unsqueeze(0).expand_as(ring))
     del scores0
     out = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+    # one zero-filled workspace for every step (each call leaves it zero)
+    ws = ets.new_workspace(w.B, w.max_len if w.api == "ragged" else w.L, w.k, dev)
     if w.api == "paged":
         lens = torch.from_numpy(w.lens).to(dev)
         pt = torch.from_numpy(w.page_table).to(dev)
 
         def step(i):
-            ets.topk_paged(ring[i % R], lens, pt, out, w.page_size)
+            ets.topk_paged(ring[i % R], lens, pt, out, w.page_size, workspace=ws)
     elif w.api == "raw":
         lens = torch.from_numpy(w.lens).to(dev) if w.lens is not None else None
 
         def step(i):
-            ets.topk_raw(ring[i % R], w.k, lens, out=out)
+            ets.topk_raw(ring[i % R], w.k, lens, out=out, workspace=ws)
     else:
         starts = torch.from_numpy(w.row_starts).to(dev)
         lengths = torch.from_numpy(w.lengths).to(dev)
         max_len = w.max_len
-        ws_bytes = ets.workspace_size(w.B, max_len, w.k)
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
         def step(i):
             ets.topk_ragged(ring[i % R], starts, lengths, w.k, max_len=max_len, out=out,

@@ -27,7 +27,8 @@ from typing import Optional
 import torch
 
 __all__ = ["topk_raw", "topk_paged", "topk_ragged", "workspace_size", "row_split",
-           "library_path", "MAX_K", "EtsError"]
+           "new_workspace", "workspace_init", "workspace_error", "library_path", "MAX_K",
+           "EtsError"]
 
 MAX_K = 2048
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -64,9 +65,10 @@ def _load():
             lib.ets_topk_ragged.argtypes = [vp, vp, vp, i32, i64, i32, vp, i64, vp, sz, vp]
             lib.ets_workspace_size.argtypes = [i32, i64, i32, i32, ctypes.POINTER(sz)]
             lib.ets_row_split.argtypes = [i32, i64, i32]
+            lib.ets_workspace_init.argtypes = [vp, sz, vp]
             lib.ets_status_string.argtypes = [i32]
             for fn in (lib.ets_topk_raw, lib.ets_topk_paged, lib.ets_topk_ragged,
-                       lib.ets_workspace_size, lib.ets_row_split):
+                       lib.ets_workspace_size, lib.ets_row_split, lib.ets_workspace_init):
                 fn.restype = ctypes.c_int32
             lib.ets_status_string.restype = ctypes.c_char_p
             _lib = lib
@@ -116,7 +118,12 @@ def _stream(device: torch.device) -> int:
 
 
 def workspace_size(B: int, max_row_len: int, k: int, device: Optional[int] = None) -> int:
-    """Bytes of workspace a call with these sizes needs (0 if none)."""
+    """Bytes of workspace a call with these sizes needs on the device (0 if none).
+
+    A workspace must be zero before its first use (``new_workspace`` or
+    ``workspace_init``); every call returns the counters and tables it relies
+    on to zero.  Calls that pass no workspace share one buffer per device and
+    stream."""
     nbytes = ctypes.c_size_t(0)
     _check(_load().ets_workspace_size(B, max_row_len, k, -1 if device is None else device,
                                       ctypes.byref(nbytes)), "ets_workspace_size")
@@ -128,6 +135,40 @@ def row_split(B: int, max_row_len: int, cu_count: int) -> int:
     return int(_load().ets_row_split(B, max_row_len, cu_count))
 
 
+# Workspace word set non-zero by a call that stopped waiting for the other
+# workgroups of a row (its results are then undefined).
+WORKSPACE_ERROR_WORD = 32
+
+# Workspaces kept per (device, stream) for calls that pass none: zero-filled
+# once, then every call returns what it relies on to zero, so one buffer
+# serves all later calls on that stream.
+_ws_cache = {}
+
+
+def new_workspace(B: int, max_row_len: int, k: int,
+                  device: Optional[torch.device] = None) -> Optional[torch.Tensor]:
+    """A zero-filled workspace for calls with these sizes (None if none is needed)."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    with torch.cuda.device(device):
+        need = workspace_size(B, max_row_len, k)
+    if need == 0:
+        return None
+    return torch.zeros(need, dtype=torch.uint8, device=device)
+
+
+def workspace_init(workspace: torch.Tensor) -> None:
+    """Zero-fills ``workspace`` on the current stream (needed once before its first use)."""
+    _require(workspace, "workspace", torch.uint8, 1)
+    with torch.cuda.device(workspace.device):
+        _check(_load().ets_workspace_init(workspace.data_ptr(), workspace.numel(),
+                                          _stream(workspace.device)), "ets_workspace_init")
+
+
+def workspace_error(workspace: torch.Tensor) -> int:
+    """The workspace's error word (synchronises); non-zero means a call timed out."""
+    return int(workspace.view(torch.int32)[WORKSPACE_ERROR_WORD].item())
+
+
 def _workspace(B: int, max_len: int, k: int, device: torch.device,
                workspace: Optional[torch.Tensor]):
     with torch.cuda.device(device):
@@ -135,7 +176,13 @@ def _workspace(B: int, max_len: int, k: int, device: torch.device,
     if need == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        key = (device.index, _stream(device))
+        with _lock:
+            workspace = _ws_cache.get(key)
+            if workspace is None or workspace.numel() < need:
+                with torch.cuda.device(device):
+                    workspace = torch.zeros(need, dtype=torch.uint8, device=device)
+                _ws_cache[key] = workspace
     if workspace.device != device or workspace.numel() * workspace.element_size() < need:
         raise ValueError("workspace must be on %s with at least %d bytes" % (device, need))
     return workspace, workspace.numel() * workspace.element_size()

@@ -42,6 +42,9 @@ constexpr int kHistBins = 1 << kHistBits;
 constexpr int kSmallCap = 128;  // largest bucket ranked by direct comparison
 constexpr int kPtCap = 2048;    // page-table entries staged in LDS
 constexpr uint32_t kPeelShare = 16;  // lanes of a wave in one bin that switch to merged atomics
+// Radix rounds needed at most: 12 + 12 + 8 key bits, then 12 + 12 + 7 position
+// bits; loops stop there even on inconsistent counts, so every kernel ends.
+constexpr int kMaxRounds = 8;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -143,15 +146,16 @@ __device__ __forceinline__ void hist_add_peel(uint32_t* hist, bool pred, uint32_
 // hist[t]) in res[0..2].  wsum[] and res[] may be reused after one more
 // barrier.
 template <int T>
+__device__ __forceinline__ void find_threshold_regs(uint32_t (&h)[kHistBins / T], uint32_t kk,
+                                                   uint32_t* wsum, uint32_t* res);
+
+template <int T>
 __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, uint32_t kk,
                                                    uint32_t bin0_less, uint32_t* wsum,
                                                    uint32_t* res) {
   constexpr int BPT = kHistBins / T;  // bins owned by each thread
-  constexpr int W = T / 64;
   static_assert(BPT * T == kHistBins && BPT % 4 == 0, "block size must divide the bins by 4");
-  const int wid = threadIdx.x >> 6;
   uint32_t h[BPT];
-  uint32_t s = 0;
 #pragma unroll
   for (int i = 0; i < BPT; i += 4) {
     const uint4 q = reinterpret_cast<const uint4*>(hist)[threadIdx.x * (BPT / 4) + i / 4];
@@ -161,6 +165,18 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, uint32_
     h[i + 3] = q.w;
   }
   if (threadIdx.x == 0) h[0] -= bin0_less;
+  find_threshold_regs<T>(h, kk, wsum, res);
+}
+
+// The search of find_threshold_bin on bins already in registers: thread t
+// holds bins [t * BPT, (t + 1) * BPT).
+template <int T>
+__device__ __forceinline__ void find_threshold_regs(uint32_t (&h)[kHistBins / T], uint32_t kk,
+                                                   uint32_t* wsum, uint32_t* res) {
+  constexpr int BPT = kHistBins / T;
+  constexpr int W = T / 64;
+  const int wid = threadIdx.x >> 6;
+  uint32_t s = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) s += h[i];
   const uint32_t incl = wave_incl_scan(s);
@@ -343,7 +359,7 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
                                       uint32_t n_pad, uint32_t probe_key, int& round) {
   uint32_t lo = in.lo, hi = in.hi, kk = in.kk, bucket = in.bucket;
   uint32_t tie = 0, dlo = 0, dhi = nm1;
-  while (bucket > static_cast<uint32_t>(kSmallCap) && lo != hi) {
+  while (bucket > static_cast<uint32_t>(kSmallCap) && lo != hi && round < kMaxRounds) {
     uint32_t* hist = sm.hist[round & 1];
     hist_clear<T>(sm.hist[(round + 1) & 1]);
     const uint32_t rlo = lo, span = hi - lo;
@@ -380,7 +396,7 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
   if (bucket > static_cast<uint32_t>(kSmallCap)) {
     tie = 1;
     const uint32_t tkey = lo;
-    while (bucket > static_cast<uint32_t>(kSmallCap)) {
+    while (bucket > static_cast<uint32_t>(kSmallCap) && round < kMaxRounds) {
       uint32_t* hist = sm.hist[round & 1];
       hist_clear<T>(sm.hist[(round + 1) & 1]);
       const uint32_t rdlo = dlo, span = dhi - dlo;
@@ -754,355 +770,507 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
   }
 }
 
-// ---------------------------------------------------------------- row-split path
+// ---------------------------------------------------------------- row-group path
 //
-// Long rows are cut into G chunks of `chunk` scores, one workgroup each
-// (after the pages' row-split path, PR #37591 topk.hip excerpt: histogram,
-// scatter and refine kernels over a workspace, the kernel boundaries acting
-// as the barriers between the chunks of a row).  Six launches:
-//   split_zero     clears the per-row records and histograms;
-//   split_bounds   per chunk: max, min of lane maxima, holders, min;
-//   split_hist     per chunk: the row's range from all chunks' bounds, a LDS
-//                  histogram of the chunk, merged into the row's histogram;
-//   split_select   per row: the threshold bin; a bucket still above
-//                  kSmallCap is refined by this workgroup streaming the row;
-//   split_scatter  per chunk: winners to the output and the bucket to the
-//                  workspace, placed through one 64-bit cursor per row;
-//   split_finish   per row: rank the bucket, emit; rows with n <= k.
-// Workspace (u32 words): rec[B][16] | part[B][G][4] | hist[B][4096] | cand[B][kSmallCap][2].
+// When the batch alone cannot fill the device, each row is cut into G
+// chunks, one workgroup each, and the G workgroups of a row run the
+// method's rounds together inside one launch (the pages' row-split path,
+// PR #37591 topk.hip excerpt, carries each row's histogram through a
+// workspace between separate kernels; here the kernel boundaries are
+// replaced by waits on per-row counters):
+//
+//  * round 0: every workgroup builds an LDS histogram of its chunk on the
+//    key's top 12 bits and adds the bins at or above its own chunk's
+//    threshold bin into the row's histogram.  The row's k-th largest key is
+//    at least any chunk's min(k, chunk)-th largest, so a bin below a chunk's
+//    threshold bin never holds the row's threshold and is not needed;
+//  * after the group's barrier every workgroup reads the row histogram and
+//    finds the same threshold bin.  A bucket larger than the tie list
+//    (scores concentrated in a few bins) is narrowed by further rounds of
+//    12-bit digits of the key, then of the position among equal keys;
+//  * every workgroup writes its winners to the output and appends its
+//    bucket members to the row's tie list, both placed through one 64-bit
+//    cursor;
+//  * the last workgroup of the group to finish ranks the tie list exactly
+//    (LDS radix rounds, then direct comparison), emits the rest of the row
+//    and returns the row's workspace to zero.
+//
+// Groups are formed in the order workgroups start (a ticket counter), so a
+// workgroup only ever waits for members that have started or start next:
+// progress needs room for one group on the device, not for the whole grid.
+// Every wait is bounded; on expiry the workspace's error word is set, the
+// call's output is undefined, and the kernel still ends.
+//
+// Data crosses workgroups only through device-scope relaxed atomics (loads
+// and stores are issued coherent at device scope, read-modify-writes are
+// performed in the memory hierarchy), with each wave's memory counter drained
+// before an arrival is counted, so no cache write-back or invalidate is
+// needed.
+//
+// Workspace (u32 words): hdr[64], then per row rec[64] | hist[3][4096] | ties[kTieCap] (u64).
+// It must be zero before its first use; every call returns the header, the
+// records and the tables to zero (tie lists may keep stale entries).
 
-constexpr int kRec = 16;
-enum RecField : int { kRecLo = 0, kRecHi, kRecKk, kRecTie, kRecDlo, kRecDhi, kRecShift, kRecPad,
-                      kRecCursor = 8 /* u64: winners << 32 | bucket entries */ };
+constexpr int kTieCap = 4096;      // tie-list entries per row
+constexpr int kGroupPtCap = 1024;  // chunk page-table entries staged in LDS
+constexpr int kRecWords = 64;      // per-row record: its own 256-byte line
+constexpr int kHdrWords = 64;
+constexpr uint32_t kSpinLimit = 1u << 20;
 
-struct SplitWs {
-  uint32_t* rec;
-  uint32_t* part;
-  uint32_t* hist;
-  uint2* cand;
-  __device__ SplitWs(uint32_t* ws, int32_t B, int32_t G) {
-    rec = ws;
-    part = rec + static_cast<int64_t>(B) * kRec;
-    hist = part + static_cast<int64_t>(B) * G * 4;
-    cand = reinterpret_cast<uint2*>(hist + static_cast<int64_t>(B) * kHistBins);
+enum HdrField : int { kHdrTicket = 0, kHdrFinished = 16, kHdrError = 32 };
+enum GroupRecField : int { kRecBarrier = 0, kRecDone = 16, kRecCursor = 32 /* u64 */, kRecTouched = 48 };
+
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class U>
+__device__ __forceinline__ U add_dev(U* p, U v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void max_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until every global access this wave issued has completed.
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Arrives at a row's barrier and returns once `target` arrivals are counted.
+// Every thread calls it; what each thread wrote before has completed by the
+// time any member leaves.
+__device__ __forceinline__ void group_sync(uint32_t* ctr, uint32_t target, uint32_t* err) {
+  drain_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t seen = add_dev(ctr, 1u) + 1u;
+    uint32_t spins = 0;
+    while (seen < target) {
+      __builtin_amdgcn_s_sleep(1);
+      seen = ld_dev(ctr);
+      if (++spins > kSpinLimit) {
+        st_dev(err, 1u);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Per-row block: record | three histogram tables | tie list.  The layout of a
+// row does not depend on the batch size, so calls of different shapes can
+// share one workspace: the tie lists, the only words left non-zero, never
+// overlap another call's counters or tables.
+constexpr int64_t kRowWords = kRecWords + 3 * kHistBins + 2 * kTieCap;
+
+struct GroupWs {
+  uint32_t* hdr;
+  __device__ explicit GroupWs(uint32_t* ws) : hdr(ws) {}
+  __device__ uint32_t* rec(int b) const { return hdr + kHdrWords + b * kRowWords; }
+  __device__ uint32_t* hist(int b) const { return rec(b) + kRecWords; }
+  __device__ uint64_t* ties(int b) const {
+    return reinterpret_cast<uint64_t*>(hist(b) + 3 * kHistBins);
   }
 };
 
-__global__ __launch_bounds__(256) void split_zero(uint32_t* ws, int32_t B, int32_t G) {
-  const SplitWs w(ws, B, G);
-  const int64_t nrec = static_cast<int64_t>(B) * kRec;
-  const int64_t nhist = static_cast<int64_t>(B) * kHistBins;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < nrec + nhist; i += 256ll * gridDim.x) {
-    if (i < nrec) w.rec[i] = 0u;
-    else w.hist[i - nrec] = 0u;
-  }
-}
-
-// Chunk g of a row: [g chunk, (g+1) chunk), the last chunk running to the
-// row's end (a ragged row may be longer than the length hint).
-__device__ __forceinline__ int32_t chunk_end(int32_t g, int32_t G, int32_t chunk, int32_t n) {
-  return g == G - 1 ? n : min(g * chunk + chunk, n);
-}
-
-// Runs body(std::true_type) when the span fits one tile (loaded once, kept
-// in registers), else body(std::false_type) (streamed per pass).
-template <class SpanT, class Body>
-__device__ __forceinline__ void with_span(const SpanT& span, typename SpanT::Keys& key, Body&& body) {
-  if (span.end - span.start <= SpanT::TILE) {
-    span.load(key, span.start);
-    body(std::true_type());
-  } else {
-    body(std::false_type());
-  }
-}
-
-template <int T, int VEC, int MODE, bool V4>
-__global__ __launch_bounds__(T) void split_bounds(Params p, uint32_t* ws, int32_t B, int32_t G,
-                                                  int32_t chunk) {
-  constexpr int W = T / 64;
-  __shared__ uint32_t red[4 * 16];
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
-  const RowRef<MODE> r(p, b);
-  if (r.n <= p.k) return;
-  const SplitWs w(ws, B, G);
-  uint32_t* part = w.part + (static_cast<int64_t>(b) * G + g) * 4;
-  const Span<T, VEC, V4> span{r.row, g * chunk, chunk_end(g, G, chunk, r.n)};
-  uint32_t key[4 * VEC];
-  if (span.start >= span.end) {
-    if (threadIdx.x == 0) {
-      part[0] = 0u;
-      part[1] = 0xFFFFFFFFu;
-      part[2] = 0u;
-      part[3] = 0xFFFFFFFFu;
-    }
-    return;
-  }
-  uint32_t m1 = 0, mn = 0xFFFFFFFFu;
-  with_span(span, key, [&](auto res) {
-    span.template for_each<decltype(res)::value>(key, [&](uint32_t x, int32_t pos, int) {
-      m1 = max(m1, x);
-      mn = min(mn, pos < span.end ? x : 0xFFFFFFFFu);
-    });
-  });
-  // a thread holds a score iff its first slot does
-  const int32_t first_pos = span.start + (V4 ? 4 * static_cast<int32_t>(threadIdx.x) : static_cast<int32_t>(threadIdx.x));
-  const bool holds = first_pos < span.end;
-  const uint32_t vmax = wave_reduce(m1, OpMax());
-  const uint32_t vmm = wave_reduce(holds ? m1 : 0xFFFFFFFFu, OpMin());
-  const uint32_t vh = wave_reduce(holds ? 1u : 0u, OpAdd());
-  const uint32_t vmin = wave_reduce(mn, OpMin());
-  const int wid = threadIdx.x >> 6;
-  if (__lane_id() == 0) {
-    red[wid] = vmax;
-    red[16 + wid] = vmm;
-    red[32 + wid] = vh;
-    red[48 + wid] = vmin;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t a = 0, bm = 0xFFFFFFFFu, c = 0, d = 0xFFFFFFFFu;
-    for (int i = 0; i < W; ++i) {
-      a = max(a, red[i]);
-      bm = min(bm, red[16 + i]);
-      c += red[32 + i];
-      d = min(d, red[48 + i]);
-    }
-    part[0] = a;
-    part[1] = bm;
-    part[2] = c;
-    part[3] = d;
-  }
-}
-
-// The row's key range from all chunks: [lower bound, max].  The lanes'
-// maxima over all chunks are `holders` distinct scores, so if they number at
-// least k their minimum bounds the k-th largest from below; otherwise the
-// row minimum does.
+// Adds the LDS bins >= from that are not zero into dst (device atomics) and
+// clears every LDS bin of the calling thread.
 template <int T>
-__device__ __forceinline__ void split_range(const uint32_t* part, int32_t G, int32_t k,
-                                            uint32_t* red, uint32_t& lo, uint32_t& hi) {
-  constexpr int W = T / 64;
-  uint32_t a = 0, bm = 0xFFFFFFFFu, c = 0, d = 0xFFFFFFFFu;
-  for (int g = threadIdx.x; g < G; g += T) {
-    const uint4 q = reinterpret_cast<const uint4*>(part)[g];
-    a = max(a, q.x);
-    bm = min(bm, q.y);
-    c += q.z;
-    d = min(d, q.w);
-  }
-  a = wave_reduce(a, OpMax());
-  bm = wave_reduce(bm, OpMin());
-  c = wave_reduce(c, OpAdd());
-  d = wave_reduce(d, OpMin());
-  const int wid = threadIdx.x >> 6;
-  if (__lane_id() == 0) {
-    red[wid] = a;
-    red[16 + wid] = bm;
-    red[32 + wid] = c;
-    red[48 + wid] = d;
-  }
-  __syncthreads();
-  a = 0, bm = 0xFFFFFFFFu, c = 0, d = 0xFFFFFFFFu;
+__device__ __forceinline__ void push_bins(uint32_t* lh, uint32_t from, uint32_t* dst) {
+  constexpr int BPT = kHistBins / T;
 #pragma unroll
-  for (int i = 0; i < W; ++i) {
-    a = max(a, red[i]);
-    bm = min(bm, red[16 + i]);
-    c += red[32 + i];
-    d = min(d, red[48 + i]);
-  }
-  hi = a;
-  lo = c >= static_cast<uint32_t>(k) ? bm : d;
-}
-
-template <int T, int VEC, int MODE, bool V4>
-__global__ __launch_bounds__(T) void split_hist(Params p, uint32_t* ws, int32_t B, int32_t G,
-                                                int32_t chunk) {
-  __shared__ __align__(16) uint32_t hist[kHistBins + 64];
-  __shared__ uint32_t red[4 * 16];
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
-  const RowRef<MODE> r(p, b);
-  if (r.n <= p.k) return;
-  const SplitWs w(ws, B, G);
-  const Span<T, VEC, V4> span{r.row, g * chunk, chunk_end(g, G, chunk, r.n)};
-  uint32_t key[4 * VEC];
-  hist_clear<T>(hist);
-  uint32_t lo, hi;
-  split_range<T>(w.part + static_cast<int64_t>(b) * G * 4, G, p.k, red, lo, hi);
-  const uint32_t span_k = hi - lo;
-  const int bl = span_k ? 32 - __clz(static_cast<int>(span_k)) : 0;
-  const int s = bl > kHistBits ? bl - kHistBits : 0;
-  uint32_t* rec = w.rec + static_cast<int64_t>(b) * kRec;
-  if (g == 0 && threadIdx.x == 0) {
-    rec[kRecLo] = lo;
-    rec[kRecHi] = hi;
-    rec[kRecShift] = static_cast<uint32_t>(s);
-  }
-  if (span.start >= span.end) return;
-  with_span(span, key, [&](auto res) {
-    constexpr bool RES = decltype(res)::value;
-    bool peel = false;
-    if (RES) {
-      const uint32_t d = key[0] - lo;
-      const uint32_t bin = d >> s;
-      const uint32_t lead = readfirstlane(bin);
-      peel = __popcll(__ballot(d <= span_k && bin == lead)) > kPeelShare;
-    }
-    if (peel) {
-      span.template for_each<RES>(key, [&](uint32_t x, int32_t, int) {
-        const uint32_t d = x - lo;
-        hist_add_peel(hist, d <= span_k, d >> s);
-      });
-    } else {
-      const uint32_t dummy = kHistBins + __lane_id();
-      span.template for_each<RES>(key, [&](uint32_t x, int32_t, int) {
-        const uint32_t d = x - lo;
-        atomicAdd(&hist[d <= span_k ? d >> s : dummy], 1u);
-      });
-    }
-  });
-  __syncthreads();
-  if (lo == 0 && threadIdx.x == 0) hist[0] -= span.pad_slots();
-  __syncthreads();
-  uint32_t* ghist = w.hist + static_cast<int64_t>(b) * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += T) {
-    const uint32_t c = hist[i];
-    if (c) __hip_atomic_fetch_add(&ghist[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < BPT; i += 4) {
+    const uint32_t b0 = threadIdx.x * BPT + i;
+    uint4* q = reinterpret_cast<uint4*>(lh + b0);
+    const uint4 c = *q;
+    *q = make_uint4(0u, 0u, 0u, 0u);
+    if (c.x != 0 && b0 >= from) add_dev(dst + b0, c.x);
+    if (c.y != 0 && b0 + 1 >= from) add_dev(dst + b0 + 1, c.y);
+    if (c.z != 0 && b0 + 2 >= from) add_dev(dst + b0 + 2, c.z);
+    if (c.w != 0 && b0 + 3 >= from) add_dev(dst + b0 + 3, c.w);
   }
 }
 
-struct alignas(16) SelectSmem {
-  SelSmem sel;
+// Reads the row histogram src and finds its threshold bin for kk (res).
+template <int T>
+__device__ __forceinline__ void read_bins(const uint32_t* src, uint32_t kk, SelSmem& ss) {
+  constexpr int BPT = kHistBins / T;
+  uint32_t h[BPT];
+#pragma unroll
+  for (int i = 0; i < BPT; i += 2) {
+    const uint64_t v = ld_dev(reinterpret_cast<const uint64_t*>(src + threadIdx.x * BPT + i));
+    h[i] = static_cast<uint32_t>(v);
+    h[i + 1] = static_cast<uint32_t>(v >> 32);
+  }
+  find_threshold_regs<T>(h, kk, ss.wsum, ss.res);
+}
+
+template <int T>
+__device__ __forceinline__ void clear_bins(uint32_t* buf, uint32_t from) {
+  for (uint32_t i = from + threadIdx.x; i < static_cast<uint32_t>(kHistBins); i += T) st_dev(buf + i, 0u);
+}
+
+// Shift that maps a range of span + 1 values onto at most kHistBins bins.
+__device__ __forceinline__ int digit_shift(uint32_t span) {
+  const int bl = span ? 32 - __clz(static_cast<int>(span)) : 0;
+  return bl > kHistBits ? bl - kHistBits : 0;
+}
+
+// The selection state after a round over digit (x - lo) >> s (keys) or
+// (n - 1 - pos - dlo) >> s (positions among equal keys) found bin res[0]
+// with res[1] entries above it and res[2] in it.
+__device__ __forceinline__ void narrow(Sel& sel, const uint32_t* res, int s) {
+  sel.kk -= res[1];
+  sel.bucket = res[2];
+  const uint32_t width = (1u << s) - 1u;
+  if (!sel.tie) {
+    sel.lo += res[0] << s;
+    if (sel.hi - sel.lo > width) sel.hi = sel.lo + width;
+  } else {
+    sel.dlo += res[0] << s;
+    if (sel.dhi - sel.dlo > width) sel.dhi = sel.dlo + width;
+  }
+}
+
+struct alignas(16) GroupSmem {
+  SelSmem sel;              // histograms (hist[0] is zero between rounds) and scan scratch
+  int32_t pt[kGroupPtCap];  // the chunk's page-table entries (paged map)
+  uint2 cand[kSmallCap];    // final bucket of the tie list
+  union {
+    int32_t pos[ETS_MAX_K];  // this workgroup's winners, in slot order
+    uint2 ties[kTieCap];     // the last workgroup: the row's tie list
+  } u;
+  uint32_t wsum2[16];
+  uint32_t ticket, last, wcount, ccount;
+  uint32_t base[2];
 };
 
-// Per row: threshold bin of the merged histogram; a bucket still above
-// kSmallCap is refined by this workgroup streaming the whole row.
-template <int T, int VEC, int MODE, bool V4>
-__global__ __launch_bounds__(T) void split_select(Params p, uint32_t* ws, int32_t B, int32_t G) {
-  __shared__ SelectSmem sm;
-  const int b = blockIdx.x;
-  const RowRef<MODE> r(p, b);
-  if (r.n <= p.k) return;
-  const SplitWs w(ws, B, G);
-  uint32_t* rec = w.rec + static_cast<int64_t>(b) * kRec;
-  const uint32_t lo = rec[kRecLo], hi = rec[kRecHi];
-  const int s = static_cast<int>(rec[kRecShift]);
-  const uint32_t* ghist = w.hist + static_cast<int64_t>(b) * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins / 4; i += T) {
-    reinterpret_cast<uint4*>(sm.sel.hist[0])[i] = reinterpret_cast<const uint4*>(ghist)[i];
-  }
-  hist_clear<T>(sm.sel.hist[1]);
-  __syncthreads();
-  find_threshold_bin<T>(sm.sel.hist[0], static_cast<uint32_t>(p.k), 0u, sm.sel.wsum, sm.sel.res);
-  Sel sel{};
-  sel.kk = static_cast<uint32_t>(p.k) - sm.sel.res[1];
-  sel.bucket = sm.sel.res[2];
-  sel.lo = lo + (sm.sel.res[0] << s);
-  sel.hi = hi;
-  sel.dhi = static_cast<uint32_t>(r.n - 1);
-  const uint32_t width = (1u << s) - 1u;
-  if (sel.hi - sel.lo > width) sel.hi = sel.lo + width;
-  if (sel.bucket > static_cast<uint32_t>(kSmallCap)) {
-    const Span<T, VEC, V4> span{r.row, 0, r.n};
-    uint32_t key[4 * VEC];
-    int round = 1;
-    sel = refine<T>([&](auto&& f) { span.template for_each<false>(key, f); }, sm.sel, sel,
-                    static_cast<uint32_t>(r.n - 1), span.pad_slots(), 0u, round);
-  }
-  if (threadIdx.x == 0) {
-    rec[kRecLo] = sel.lo;
-    rec[kRecHi] = sel.hi;
-    rec[kRecKk] = sel.kk;
-    rec[kRecTie] = sel.tie;
-    rec[kRecDlo] = sel.dlo;
-    rec[kRecDhi] = sel.dhi;
-  }
-}
-
-template <int T, int VEC, int MODE, bool V4>
-__global__ __launch_bounds__(T) void split_scatter(Params p, uint32_t* ws, int32_t B, int32_t G,
-                                                   int32_t chunk) {
+// One chunk [span.start, span.end) of row b as member g of its row's group.
+// RES: the chunk fits one tile and stays in registers; otherwise every pass
+// streams it.
+template <int T, int VEC, int MODE, bool V4, bool RES>
+__device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const GroupWs& w,
+                                          const RowRef<MODE>& r, int b, int g, int G,
+                                          const Span<T, VEC, V4>& span) {
+  constexpr int PT = Span<T, VEC, V4>::PT;
   constexpr int W = T / 64;
-  __shared__ uint32_t wsum[16];
-  __shared__ uint32_t base[2];
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
-  const RowRef<MODE> r(p, b);
-  if (r.n <= p.k) return;
-  const SplitWs w(ws, B, G);
-  uint32_t* rec = w.rec + static_cast<int64_t>(b) * kRec;
-  const Span<T, VEC, V4> span{r.row, g * chunk, chunk_end(g, G, chunk, r.n)};
-  uint32_t key[4 * VEC];
-  if (span.start >= span.end) return;
-  Sel sel{};
-  sel.lo = rec[kRecLo];
-  sel.hi = rec[kRecHi];
-  sel.kk = rec[kRecKk];
-  sel.tie = rec[kRecTie];
-  sel.dlo = rec[kRecDlo];
-  sel.dhi = rec[kRecDhi];
-  const uint32_t nm1 = static_cast<uint32_t>(r.n - 1);
-  const uint32_t first = static_cast<uint32_t>(p.k) - sel.kk;
-  uint2* cand = w.cand + static_cast<int64_t>(b) * kSmallCap;
-  with_span(span, key, [&](auto res) {
-    constexpr bool RES = decltype(res)::value;
-    uint32_t nw = 0, nc = 0;
-    span.template for_each<RES>(key, [&](uint32_t x, int32_t pos, int) {
-      nw += sel_winner(sel, nm1, span.end, x, pos) ? 1u : 0u;
-      nc += sel_bucket(sel, nm1, span.end, x, pos) ? 1u : 0u;
-    });
-    // one scan of (winners | bucket << 16): a chunk has fewer than 2^16 of each
-    const uint32_t packed = nw | (nc << 16);
-    const uint32_t incl = wave_incl_scan(packed);
-    const int wid = threadIdx.x >> 6;
-    if (__lane_id() == 63) wsum[wid] = incl;
-    __syncthreads();
-    uint32_t off = incl - packed, tot = 0;
+  const int tid = threadIdx.x;
+  const int wid = tid >> 6;
+  const int32_t k = p.k;
+  const int32_t n = r.n;
+  const uint32_t nm1 = static_cast<uint32_t>(n - 1);
+  uint32_t* rec = w.rec(b);
+  uint32_t* ghist = w.hist(b);
+  uint64_t* gties = w.ties(b);
+  uint32_t* err = w.hdr + kHdrError;
+  uint32_t* lh = sm.sel.hist[0];  // cleared below, then zero again after every push
+
+  uint32_t key[PT];
+  if constexpr (RES) span.load(key, span.start);
+  auto for_each = [&](auto&& f) { span.template for_each<RES>(key, f); };
+  // the chunk's page ids, fetched after the scores and kept in registers
+  // until the winners are emitted, so that no wait on them delays the rounds
+  constexpr int PTV = (MODE == kPaged) ? (kGroupPtCap + T - 1) / T : 1;
+  int32_t ptv[PTV];
+  int32_t p0 = 0, np = 0;
+  bool pt_lds = false;
+  if constexpr (MODE == kPaged) {
+    if (p.page_shift >= 0 && span.end > span.start) {
+      p0 = span.start >> p.page_shift;
+      np = ((span.end - 1) >> p.page_shift) - p0 + 1;
+      pt_lds = np <= kGroupPtCap;
+      if (pt_lds) {
 #pragma unroll
-    for (int i = 0; i < W; ++i) {
-      off += (i < wid) ? wsum[i] : 0u;
-      tot += wsum[i];
+        for (int i = 0; i < PTV; ++i) ptv[i] = (tid + i * T < np) ? r.pt_row[p0 + tid + i * T] : 0;
+      }
     }
-    if (threadIdx.x == 0) {
-      const uint64_t add = (static_cast<uint64_t>(tot & 0xFFFFu) << 32) | (tot >> 16);
-      const uint64_t old = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(rec + kRecCursor), add,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      base[0] = static_cast<uint32_t>(old >> 32);
-      base[1] = static_cast<uint32_t>(old);
+  }
+  hist_clear<T>(lh);
+  __syncthreads();
+  const uint32_t pad = span.pad_slots();
+  const int32_t nc = span.end - span.start;
+
+  // ---- round 0: top 12 key bits
+  {
+    const uint32_t probe = RES ? key[0] >> 20 : 0u;
+    const bool peel = __popcll(__ballot(probe == readfirstlane(probe))) > kPeelShare;
+    if (peel) {
+      for_each([&](uint32_t x, int32_t, int) { hist_add_peel(lh, true, x >> 20); });
+    } else {
+      for_each([&](uint32_t x, int32_t, int) { atomicAdd(&lh[x >> 20], 1u); });
     }
     __syncthreads();
-    uint32_t wo = base[0] + (off & 0xFFFFu);
-    uint32_t co = base[1] + (off >> 16);
-    span.template for_each<RES>(key, [&](uint32_t x, int32_t pos, int) {
-      if (sel_winner(sel, nm1, span.end, x, pos)) {
-        if (wo < first) r.out[wo] = out_value<MODE>(p, false, nullptr, r.pt_row, r.row_start, pos);
-        ++wo;
+    if (tid == 0) lh[0] -= pad;  // padding slots hold key 0
+    __syncthreads();
+  }
+  uint32_t from = kHistBins;
+  if (nc > 0) {
+    find_threshold_bin<T>(lh, static_cast<uint32_t>(min(k, nc)), 0u, sm.sel.wsum, sm.sel.res);
+    from = sm.sel.res[0];
+  }
+  if (tid == 0 && from < static_cast<uint32_t>(kHistBins)) max_dev(rec + kRecTouched, kHistBins - from);
+  push_bins<T>(lh, from, ghist);
+  group_sync(rec + kRecBarrier, static_cast<uint32_t>(G), err);
+  Sel sel{};
+  sel.lo = 0u;
+  sel.hi = 0xFFFFFFFFu;
+  sel.kk = static_cast<uint32_t>(k);
+  sel.dlo = 0u;
+  sel.dhi = nm1;
+  read_bins<T>(ghist, sel.kk, sm.sel);
+  narrow(sel, sm.sel.res, 32 - kHistBits);
+
+  // ---- further rounds while the bucket exceeds the tie list
+  int round = 1;
+  while (sel.bucket > static_cast<uint32_t>(kTieCap) && round < kMaxRounds) {
+    uint32_t* buf = ghist + (round % 3) * kHistBins;
+    if (!sel.tie && sel.lo == sel.hi) sel.tie = 1;
+    int s;
+    if (!sel.tie) {
+      const uint32_t lo = sel.lo, span_k = sel.hi - sel.lo;
+      s = digit_shift(span_k);
+      const uint32_t pd = (RES ? key[0] : 0u) - lo;
+      const uint32_t pbin = pd >> s;
+      const bool peel = __popcll(__ballot(pd <= span_k && pbin == readfirstlane(pbin))) > kPeelShare;
+      if (peel) {
+        for_each([&](uint32_t x, int32_t, int) {
+          const uint32_t d = x - lo;
+          hist_add_peel(lh, d <= span_k, d >> s);
+        });
+      } else {
+        const uint32_t dummy = kHistBins + __lane_id();
+        for_each([&](uint32_t x, int32_t, int) {
+          const uint32_t d = x - lo;
+          atomicAdd(&lh[d <= span_k ? d >> s : dummy], 1u);
+        });
       }
-      if (sel_bucket(sel, nm1, span.end, x, pos)) {
-        if (co < static_cast<uint32_t>(kSmallCap)) cand[co] = make_uint2(x, static_cast<uint32_t>(pos));
-        ++co;
+      __syncthreads();
+      if (lo == 0 && tid == 0) lh[0] -= pad;
+    } else {
+      const uint32_t tkey = sel.hi, dlo = sel.dlo, span_d = sel.dhi - sel.dlo;
+      s = digit_shift(span_d);
+      const int32_t end = span.end;
+      for_each([&](uint32_t x, int32_t pos, int) {
+        const uint32_t d = nm1 - static_cast<uint32_t>(pos) - dlo;
+        hist_add_peel(lh, x == tkey && pos < end && d <= span_d, d >> s);
+      });
+    }
+    __syncthreads();
+    push_bins<T>(lh, 0u, buf);
+    group_sync(rec + kRecBarrier, static_cast<uint32_t>(G) * (round + 1), err);
+    if (g == 0) {
+      // the previous round's table is read by every member by now and is next
+      // used two rounds on, after this member's next arrival
+      const int prev = round - 1;
+      clear_bins<T>(ghist + (prev % 3) * kHistBins,
+                    prev == 0 ? kHistBins - ld_dev(rec + kRecTouched) : 0u);
+    }
+    read_bins<T>(buf, sel.kk, sm.sel);
+    narrow(sel, sm.sel.res, s);
+    ++round;
+  }
+
+  // ---- scatter: winners to the output, bucket members to the tie list
+  if constexpr (MODE == kPaged) {
+    if (pt_lds) {
+#pragma unroll
+      for (int i = 0; i < PTV; ++i)
+        if (tid + i * T < np) sm.pt[tid + i * T] = ptv[i];
+    }
+  }
+  const uint32_t first = static_cast<uint32_t>(k) - sel.kk;  // winners of the whole row
+  const int32_t cend = span.end;
+  uint32_t nw = 0, nb = 0;
+  uint32_t wmask = 0, cmask = 0;  // RES: bit PT-1-j marks slot j
+  if constexpr (RES) {
+    static_assert(PT <= 32, "slot masks are 32 bits");
+    for_each([&](uint32_t x, int32_t pos, int) {
+      wmask = wmask + wmask + (sel_winner(sel, nm1, cend, x, pos) ? 1u : 0u);
+      cmask = cmask + cmask + (sel_bucket(sel, nm1, cend, x, pos) ? 1u : 0u);
+    });
+    nw = static_cast<uint32_t>(__popc(wmask));
+    nb = static_cast<uint32_t>(__popc(cmask));
+  } else {
+    for_each([&](uint32_t x, int32_t pos, int) {
+      nw += sel_winner(sel, nm1, cend, x, pos) ? 1u : 0u;
+      nb += sel_bucket(sel, nm1, cend, x, pos) ? 1u : 0u;
+    });
+  }
+  const uint32_t iw = wave_incl_scan(nw);
+  const uint32_t ib = wave_incl_scan(nb);
+  if (__lane_id() == 63) {
+    sm.sel.wsum[wid] = iw;
+    sm.wsum2[wid] = ib;
+  }
+  __syncthreads();
+  uint32_t ow = iw - nw + sum_other_waves<W, true>(sm.sel.wsum);
+  uint32_t ob = ib - nb + sum_other_waves<W, true>(sm.wsum2);
+  if (tid == T - 1) {
+    const uint64_t add = (static_cast<uint64_t>(ow + nw) << 32) | (ob + nb);
+    const uint64_t old = add_dev(reinterpret_cast<uint64_t*>(rec + kRecCursor), add);
+    sm.base[0] = static_cast<uint32_t>(old >> 32);
+    sm.base[1] = static_cast<uint32_t>(old);
+    sm.wcount = ow + nw;
+  }
+  __syncthreads();
+  const uint32_t wbase = sm.base[0];
+  const uint32_t wtot = sm.wcount;
+  ob += sm.base[1];
+  if constexpr (RES) {
+    while (wmask != 0) {
+      const int j = PT - __ffs(static_cast<int>(wmask));
+      wmask &= wmask - 1u;
+      if (ow < static_cast<uint32_t>(ETS_MAX_K)) sm.u.pos[ow] = span.start + tile_pos<T, V4>(j);
+      ++ow;
+    }
+    while (cmask != 0) {
+      const int j = PT - __ffs(static_cast<int>(cmask));
+      cmask &= cmask - 1u;
+      const uint32_t pos = static_cast<uint32_t>(span.start + tile_pos<T, V4>(j));
+      if (ob < static_cast<uint32_t>(kTieCap))
+        st_dev(gties + ob, (static_cast<uint64_t>(select_slot<PT>(key, j)) << 32) | pos);
+      ++ob;
+    }
+  } else {
+    for_each([&](uint32_t x, int32_t pos, int) {
+      if (sel_winner(sel, nm1, cend, x, pos)) {
+        if (ow < static_cast<uint32_t>(ETS_MAX_K)) sm.u.pos[ow] = pos;
+        ++ow;
+      }
+      if (sel_bucket(sel, nm1, cend, x, pos)) {
+        if (ob < static_cast<uint32_t>(kTieCap))
+          st_dev(gties + ob, (static_cast<uint64_t>(x) << 32) | static_cast<uint32_t>(pos));
+        ++ob;
       }
     });
+  }
+  __syncthreads();
+  // winners through the output map, contiguous stores
+  auto map_any = [&](int32_t pos) {
+    return out_value<MODE>(p, false, nullptr, r.pt_row, r.row_start, pos);
+  };
+  if (MODE == kPaged && pt_lds) {
+    const int32_t ps = p.page_size, sh = p.page_shift;
+    for (uint32_t i = tid; i < wtot; i += T) {
+      const uint32_t slot = wbase + i;
+      if (slot < first && i < static_cast<uint32_t>(ETS_MAX_K)) {
+        const int32_t pos = sm.u.pos[i];
+        r.out[slot] = ((lds_i32*)sm.pt)[(pos >> sh) - p0] * ps + (pos & (ps - 1));
+      }
+    }
+  } else {
+    for (uint32_t i = tid; i < wtot; i += T) {
+      const uint32_t slot = wbase + i;
+      if (slot < first && i < static_cast<uint32_t>(ETS_MAX_K)) r.out[slot] = map_any(sm.u.pos[i]);
+    }
+  }
+
+  // ---- the group's last workgroup resolves the tie list
+  drain_vmem();
+  __syncthreads();
+  if (tid == 0) sm.last = (add_dev(rec + kRecDone, 1u) == static_cast<uint32_t>(G - 1)) ? 1u : 0u;
+  __syncthreads();
+  if (!sm.last) return;
+  const uint32_t m = min(static_cast<uint32_t>(ld_dev(reinterpret_cast<const uint64_t*>(rec + kRecCursor))),
+                         static_cast<uint32_t>(kTieCap));
+  for (uint32_t i = tid; i < m; i += T) {
+    const uint64_t v = ld_dev(gties + i);
+    sm.u.ties[i] = make_uint2(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(v));
+  }
+  if (tid == 0) {
+    sm.wcount = 0;
+    sm.ccount = 0;
+  }
+  __syncthreads();
+  const int trips = static_cast<int>((m + T - 1) / T);
+  const uint32_t tpad = static_cast<uint32_t>(trips) * T - m;
+  // every lane visits the same number of slots (the radix rounds vote per wave);
+  // slots past the list read as key 0 at position n
+  auto for_ties = [&](auto&& f) {
+    for (int j = 0; j < trips; ++j) {
+      const uint32_t i = static_cast<uint32_t>(j * T + tid);
+      const bool v = i < m;
+      const uint2 e = sm.u.ties[v ? i : 0u];
+      f(v ? e.x : 0u, v ? static_cast<int32_t>(e.y) : n, j);
+    }
+  };
+  int lround = 0;
+  const Sel fin = refine<T>(for_ties, sm.sel, sel, nm1, tpad, sm.u.ties[min(static_cast<uint32_t>(tid), m > 0 ? m - 1 : 0u)].x,
+                            lround);
+  const uint32_t first2 = first + (sel.kk - fin.kk);
+  for_ties([&](uint32_t x, int32_t pos, int) {
+    if (pos >= n) return;
+    if (sel_winner(fin, nm1, n, x, pos)) {
+      const uint32_t slot = first + atomicAdd(&sm.wcount, 1u);
+      if (slot < first2) r.out[slot] = map_any(pos);
+    } else if (sel_bucket(fin, nm1, n, x, pos)) {
+      const uint32_t c = atomicAdd(&sm.ccount, 1u);
+      if (c < static_cast<uint32_t>(kSmallCap)) sm.cand[c] = make_uint2(x, static_cast<uint32_t>(pos));
+    }
   });
+  __syncthreads();
+  rank_bucket<T>(sm.cand, min(sm.ccount, static_cast<uint32_t>(kSmallCap)), fin.kk, first2,
+                 [&](uint32_t slot, int32_t pos) { r.out[slot] = map_any(pos); });
+
+  // ---- return the row's workspace to zero: the last round's table (round 0:
+  // only its touched range; earlier rounds were cleared on the way) and the record
+  const uint32_t touched = ld_dev(rec + kRecTouched);
+  const int lastr = round - 1;
+  clear_bins<T>(ghist + (lastr % 3) * kHistBins, lastr == 0 ? kHistBins - touched : 0u);
+  __syncthreads();  // every wave has read the record before it is reset
+  if (tid == 0) {
+    st_dev(rec + kRecBarrier, 0u);
+    st_dev(rec + kRecDone, 0u);
+    st_dev(reinterpret_cast<uint64_t*>(rec + kRecCursor), 0ull);
+    st_dev(rec + kRecTouched, 0u);
+  }
 }
 
-template <int T, int MODE>
-__global__ __launch_bounds__(T) void split_finish(Params p, uint32_t* ws, int32_t B, int32_t G) {
-  __shared__ uint2 cand[kSmallCap];
-  const int b = blockIdx.x;
-  const RowRef<MODE> r(p, b);
-  if (r.n <= p.k) {
-    emit_whole_row<T, MODE>(p, r);
-    return;
-  }
-  const SplitWs w(ws, B, G);
-  const uint32_t* rec = w.rec + static_cast<int64_t>(b) * kRec;
-  const uint32_t kk = rec[kRecKk];
-  const uint32_t nc = min(rec[kRecCursor], static_cast<uint32_t>(kSmallCap));
-  const uint2* gc = w.cand + static_cast<int64_t>(b) * kSmallCap;
-  for (uint32_t i = threadIdx.x; i < nc; i += T) cand[i] = gc[i];
+// One launch for the whole batch: B * G workgroups, G per row.
+template <int T, int VEC, int MODE, bool V4>
+__global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, int32_t B, int32_t G) {
+  __shared__ GroupSmem sm;
+  const GroupWs w(ws);
+  if (threadIdx.x == 0) sm.ticket = add_dev(w.hdr + kHdrTicket, 1u);
   __syncthreads();
-  rank_bucket<T>(cand, nc, kk, static_cast<uint32_t>(p.k) - kk, [&](uint32_t slot, int32_t pos) {
-    r.out[slot] = out_value<MODE>(p, false, nullptr, r.pt_row, r.row_start, pos);
-  });
+  const uint32_t ticket = sm.ticket;
+  const int b = static_cast<int>(ticket / static_cast<uint32_t>(G));
+  const int g = static_cast<int>(ticket % static_cast<uint32_t>(G));
+  if (b < B) {  // always, unless the workspace was not zero
+    const RowRef<MODE> r(p, b);
+    if (r.n <= p.k) {
+      if (g == 0) emit_whole_row<T, MODE>(p, r);
+    } else {
+      using SpanT = Span<T, VEC, V4>;
+      const int64_t chunk = ((static_cast<int64_t>(r.n) + G - 1) / G + 3) & ~static_cast<int64_t>(3);
+      const int32_t start = static_cast<int32_t>(min(static_cast<int64_t>(g) * chunk, static_cast<int64_t>(r.n)));
+      const int32_t end = (g == G - 1) ? r.n : static_cast<int32_t>(min(start + chunk, static_cast<int64_t>(r.n)));
+      const SpanT span{r.row, start, end};
+      if (end - start <= SpanT::TILE) {
+        group_row<T, VEC, MODE, V4, true>(p, sm, w, r, b, g, G, span);
+      } else {
+        group_row<T, VEC, MODE, V4, false>(p, sm, w, r, b, g, G, span);
+      }
+    }
+  }
+  // the last workgroup to finish re-arms the ticket counter for the next call
+  drain_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0 && add_dev(w.hdr + kHdrFinished, 1u) == gridDim.x - 1) {
+    st_dev(w.hdr + kHdrTicket, 0u);
+    st_dev(w.hdr + kHdrFinished, 0u);
+  }
+}
+
+// Zero-fills a workspace (words of 4 bytes).
+__global__ __launch_bounds__(256) void workspace_clear(uint32_t* ws, int64_t words) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < words; i += 256ll * gridDim.x) ws[i] = 0u;
 }
 
 }  // namespace ets
@@ -1121,9 +1289,8 @@ constexpr int kMaxDevices = 64;
 std::mutex g_dev_mutex;
 DeviceInfo g_dev[kMaxDevices];
 
-ets_status current_device(int* dev_out, DeviceInfo* info_out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ETS_ERR_DEVICE;
+ets_status device_info(int dev, DeviceInfo* info_out) {
+  if (dev < 0 || dev >= kMaxDevices) return ETS_ERR_DEVICE;
   std::lock_guard<std::mutex> lock(g_dev_mutex);
   DeviceInfo& d = g_dev[dev];
   if (!d.queried) {
@@ -1134,9 +1301,15 @@ ets_status current_device(int* dev_out, DeviceInfo* info_out) {
     d.queried = true;
   }
   if (!d.supported) return ETS_ERR_DEVICE;
-  *dev_out = dev;
   *info_out = d;
   return ETS_OK;
+}
+
+ets_status current_device(int* dev_out, DeviceInfo* info_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ETS_ERR_DEVICE;
+  *dev_out = dev;
+  return device_info(dev, info_out);
 }
 
 int32_t page_shift_of(int32_t ps) {
@@ -1150,50 +1323,47 @@ constexpr int kRowThreads = 1024;
 constexpr int kRowVec = 8;  // 8 x float4 per lane -> 32768 scores per tile
 constexpr int64_t kRowTile = static_cast<int64_t>(kRowThreads) * 4 * kRowVec;
 
-// row-split path: chunk workgroups of 256 lanes x 16 scores, per-row kernels of 1024 lanes
-constexpr int kSplitThreads = 256;
-constexpr int kSplitVec = 4;
-constexpr int64_t kSplitChunk = static_cast<int64_t>(kSplitThreads) * 4 * kSplitVec;  // 4096
-constexpr int kSelThreads = 1024;
-constexpr int kSelVec = 8;
+// row-group path: 1024-lane workgroups, each holding up to VEC float4 per lane
+constexpr int kGroupThreads = 1024;
+constexpr int64_t kGroupChunk = 8192;  // scores per workgroup of a split row
+constexpr int64_t kMaxGroup = 64;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-// Chunks per row (0 = one workgroup per row).  A row that fits one resident
-// tile stays on one workgroup; longer rows are cut into kSplitChunk chunks.
-// ETS_ROW_SPLIT = 0 disables splitting; a positive value forces that many
-// chunks per row.
-int32_t split_plan(int32_t B, int64_t max_len) {
-  (void)B;
+// Workgroups per row (0 = one workgroup per row on the row kernel).  A row
+// that fits one resident 32768-score tile stays on one workgroup: measured on
+// MI355X, the group's exchanges cost more than the work they spread.  Longer
+// rows are cut into chunks of about kGroupChunk scores, at most kMaxGroup per
+// row.  ETS_ROW_SPLIT overrides: 0 or 1 = one workgroup per row, n >= 2 = n
+// workgroups per row (at most kMaxGroup).  The compute-unit count is part of
+// the interface for heuristics that weigh it; this one does not need it.
+int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count) {
+  (void)cu_count;
+  if (B <= 0 || max_len <= 0) return 0;
   if (const char* e = std::getenv("ETS_ROW_SPLIT"); e != nullptr && *e != '\0') {
     char* end = nullptr;
     const long v = std::strtol(e, &end, 10);
-    if (end != e && *end == '\0' && v >= 0 && v <= 65536) {
-      if (v == 0 || max_len <= 0) return 0;
-      return static_cast<int32_t>(std::min<int64_t>(v, (max_len + 3) / 4));
+    if (end != e && *end == '\0' && v >= 0) {
+      if (v <= 1) return 0;
+      return static_cast<int32_t>(std::min<int64_t>(v, kMaxGroup));
     }
   }
   if (max_len <= kRowTile) return 0;
-  return static_cast<int32_t>((max_len + kSplitChunk - 1) / kSplitChunk);
+  return static_cast<int32_t>(std::min((max_len + kGroupChunk - 1) / kGroupChunk, kMaxGroup));
 }
 
-int32_t split_chunk(int64_t max_len, int32_t G) {
-  const int64_t c = (max_len + G - 1) / G;
-  return static_cast<int32_t>((c + 3) / 4 * 4);
+size_t group_ws_bytes(int32_t B) {
+  const size_t per_row = ets::kRecWords + 3 * static_cast<size_t>(ets::kHistBins) + 2 * static_cast<size_t>(ets::kTieCap);
+  return (ets::kHdrWords + static_cast<size_t>(B) * per_row) * 4;
 }
 
-size_t split_ws_bytes(int32_t B, int32_t G) {
-  const size_t words = static_cast<size_t>(B) *
-                       (ets::kRec + 4 * static_cast<size_t>(G) + ets::kHistBins + 2 * ets::kSmallCap);
-  return (words * 4 + 255) / 256 * 256;
-}
-
-// Host-side check of the split path's workspace, before any HIP call.
-ets_status check_workspace(int32_t B, int64_t max_len, const void* ws, size_t ws_bytes) {
-  const int32_t G = split_plan(B, max_len);
+// Host-side check of the row-group path's workspace, before anything is enqueued.
+ets_status check_workspace(int32_t B, int64_t max_len, int32_t cu_count, const void* ws,
+                           size_t ws_bytes) {
+  const int32_t G = split_plan(B, max_len, cu_count);
   if (G == 0) return ETS_OK;
   if (static_cast<int64_t>(B) * G > INT32_MAX) return ETS_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < split_ws_bytes(B, G) || !aligned16(ws)) return ETS_ERR_WORKSPACE;
+  if (!ws || ws_bytes < group_ws_bytes(B) || !aligned16(ws)) return ETS_ERR_WORKSPACE;
   return ETS_OK;
 }
 
@@ -1203,12 +1373,18 @@ void launch_rows(const ets::Params& p, int32_t B, hipStream_t stream) {
                      p);
 }
 
+template <int MODE, bool V4, int VEC>
+void launch_group(const ets::Params& p, int32_t B, int32_t G, void* ws, hipStream_t stream) {
+  hipLaunchKernelGGL((ets::group_topk_kernel<kGroupThreads, VEC, MODE, V4>),
+                     dim3(static_cast<uint32_t>(B) * static_cast<uint32_t>(G)), dim3(kGroupThreads),
+                     0, stream, p, static_cast<uint32_t*>(ws), B, G);
+}
+
 template <int MODE, bool V4>
-ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, void* ws, size_t ws_bytes,
+ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, int32_t cu_count, void* ws,
                   hipStream_t stream) {
-  const int32_t G = split_plan(B, max_len);
+  const int32_t G = split_plan(B, max_len, cu_count);
   if (G == 0) {
-    // the smallest resident tile (1024 lanes x 4 VEC scores) that holds the row
     // the smallest resident tile that holds the row, with as few scores per
     // lane as the lane count allows: the passes are latency bound, and more
     // waves with shorter slot loops hide more of it
@@ -1228,22 +1404,16 @@ ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, void* ws, si
     return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
   }
   // (workspace already validated by check_workspace)
-  const int32_t chunk = split_chunk(max_len, G);
-  auto* w = static_cast<uint32_t*>(ws);
-  const int64_t zero_words = static_cast<int64_t>(B) * (ets::kRec + ets::kHistBins);
-  const int zero_blocks = static_cast<int>(std::min<int64_t>(1024, (zero_words + 255) / 256));
-  const dim3 chunks(static_cast<uint32_t>(B) * G), rows(B);
-  hipLaunchKernelGGL(ets::split_zero, dim3(zero_blocks), dim3(256), 0, stream, w, B, G);
-  hipLaunchKernelGGL((ets::split_bounds<kSplitThreads, kSplitVec, MODE, V4>), chunks,
-                     dim3(kSplitThreads), 0, stream, p, w, B, G, chunk);
-  hipLaunchKernelGGL((ets::split_hist<kSplitThreads, kSplitVec, MODE, V4>), chunks,
-                     dim3(kSplitThreads), 0, stream, p, w, B, G, chunk);
-  hipLaunchKernelGGL((ets::split_select<kSelThreads, kSelVec, MODE, V4>), rows, dim3(kSelThreads),
-                     0, stream, p, w, B, G);
-  hipLaunchKernelGGL((ets::split_scatter<kSplitThreads, kSplitVec, MODE, V4>), chunks,
-                     dim3(kSplitThreads), 0, stream, p, w, B, G, chunk);
-  hipLaunchKernelGGL((ets::split_finish<kSelThreads, MODE>), rows, dim3(kSelThreads), 0, stream, p,
-                     w, B, G);
+  const int64_t chunk = ((max_len + G - 1) / G + 3) / 4 * 4;
+  if (chunk <= kGroupThreads * 4) {
+    launch_group<MODE, V4, 1>(p, B, G, ws, stream);
+  } else if (chunk <= kGroupThreads * 8) {
+    launch_group<MODE, V4, 2>(p, B, G, ws, stream);
+  } else if (chunk <= kGroupThreads * 16) {
+    launch_group<MODE, V4, 4>(p, B, G, ws, stream);
+  } else {
+    launch_group<MODE, V4, 8>(p, B, G, ws, stream);
+  }
   return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
 }
 
@@ -1264,18 +1434,30 @@ const char* ets_status_string(ets_status status) {
 }
 
 int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count) {
-  (void)cu_count;
-  return split_plan(B, max_row_len);
+  return split_plan(B, max_row_len, cu_count);
 }
 
 ets_status ets_workspace_size(int32_t B, int64_t max_row_len, int32_t k, int32_t device,
                               size_t* bytes) {
   if (!bytes || B < 0 || max_row_len < 0) return ETS_ERR_INVALID_ARG;
   if (k < 1 || k > ETS_MAX_K) return ETS_ERR_K_RANGE;
-  (void)device;
-  const int32_t G = split_plan(B, max_row_len);
-  *bytes = (G == 0 || B == 0) ? 0 : split_ws_bytes(B, G);
+  DeviceInfo info;
+  int dev = device;
+  if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return ETS_ERR_DEVICE;
+  if (ets_status st = device_info(dev, &info); st != ETS_OK) return st;
+  const int32_t G = split_plan(B, max_row_len, info.cu_count);
+  *bytes = (G == 0 || B == 0) ? 0 : group_ws_bytes(B);
   return ETS_OK;
+}
+
+ets_status ets_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes == 0) return ETS_OK;
+  if (!workspace || !aligned16(workspace)) return ETS_ERR_INVALID_ARG;
+  const int64_t words = static_cast<int64_t>(workspace_bytes / 4);
+  const int blocks = static_cast<int>(std::min<int64_t>(1024, (words + 255) / 256));
+  hipLaunchKernelGGL(ets::workspace_clear, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint32_t*>(workspace), words);
+  return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
 }
 
 ets_status ets_topk_raw(const float* scores, int64_t row_stride, int32_t B, int32_t L,
@@ -1285,10 +1467,11 @@ ets_status ets_topk_raw(const float* scores, int64_t row_stride, int32_t B, int3
   if (B < 0 || L < 0 || row_stride < L || out_stride < k) return ETS_ERR_INVALID_ARG;
   if (B == 0) return ETS_OK;
   if (!out || (L > 0 && !scores)) return ETS_ERR_INVALID_ARG;
-  if (ets_status st = check_workspace(B, L, workspace, workspace_bytes); st != ETS_OK) return st;
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
+  if (ets_status st = check_workspace(B, L, info.cu_count, workspace, workspace_bytes); st != ETS_OK)
+    return st;
   ets::Params p{};
   p.scores = scores;
   p.row_stride = row_stride;
@@ -1300,8 +1483,8 @@ ets_status ets_topk_raw(const float* scores, int64_t row_stride, int32_t B, int3
   p.page_shift = -1;
   const bool v4 = aligned16(scores) && (row_stride % 4 == 0) && (L % 4 == 0);
   auto s = static_cast<hipStream_t>(stream);
-  return v4 ? launch<ets::kRaw, true>(p, B, L, workspace, workspace_bytes, s)
-            : launch<ets::kRaw, false>(p, B, L, workspace, workspace_bytes, s);
+  return v4 ? launch<ets::kRaw, true>(p, B, L, info.cu_count, workspace, s)
+            : launch<ets::kRaw, false>(p, B, L, info.cu_count, workspace, s);
 }
 
 ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, int32_t L,
@@ -1313,10 +1496,11 @@ ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, in
     return ETS_ERR_INVALID_ARG;
   if (B == 0) return ETS_OK;
   if (!out || !seq_lens || !page_table || (L > 0 && !scores)) return ETS_ERR_INVALID_ARG;
-  if (ets_status st = check_workspace(B, L, workspace, workspace_bytes); st != ETS_OK) return st;
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
+  if (ets_status st = check_workspace(B, L, info.cu_count, workspace, workspace_bytes); st != ETS_OK)
+    return st;
   ets::Params p{};
   p.scores = scores;
   p.row_stride = row_stride;
@@ -1331,8 +1515,8 @@ ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, in
   p.out_stride = out_stride;
   const bool v4 = aligned16(scores) && (row_stride % 4 == 0) && (L % 4 == 0);
   auto s = static_cast<hipStream_t>(stream);
-  return v4 ? launch<ets::kPaged, true>(p, B, L, workspace, workspace_bytes, s)
-            : launch<ets::kPaged, false>(p, B, L, workspace, workspace_bytes, s);
+  return v4 ? launch<ets::kPaged, true>(p, B, L, info.cu_count, workspace, s)
+            : launch<ets::kPaged, false>(p, B, L, info.cu_count, workspace, s);
 }
 
 ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,
@@ -1343,11 +1527,12 @@ ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,
   if (B < 0 || max_len_hint < 0 || out_stride < k) return ETS_ERR_INVALID_ARG;
   if (B == 0) return ETS_OK;
   if (!out || !row_starts || !lengths || !packed) return ETS_ERR_INVALID_ARG;
-  if (ets_status st = check_workspace(B, max_len_hint, workspace, workspace_bytes); st != ETS_OK)
-    return st;
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
+  if (ets_status st = check_workspace(B, max_len_hint, info.cu_count, workspace, workspace_bytes);
+      st != ETS_OK)
+    return st;
   ets::Params p{};
   p.scores = packed;
   p.lens = lengths;
@@ -1356,7 +1541,7 @@ ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,
   p.out = out;
   p.out_stride = out_stride;
   p.page_shift = -1;
-  return launch<ets::kRagged, false>(p, B, max_len_hint, workspace, workspace_bytes,
+  return launch<ets::kRagged, false>(p, B, max_len_hint, info.cu_count, workspace,
                                      static_cast<hipStream_t>(stream));
 }
 

@@ -17,7 +17,8 @@
  * Output (sglang PR #36004 digest, test excerpt; PR #37591 digest, the
  * CoopParams / OutMap excerpt): each row of `out` receives m = min(k, n)
  * mapped positions followed by k - m entries of -1.  The m entries appear in
- * an unspecified (but run-to-run deterministic) order; compare them as sets.
+ * an unspecified order, which may change from run to run when a row is split
+ * over several workgroups (the set never does); compare them as sets.
  * Every one of the k slots is written; prior contents of `out` do not matter.
  * Position maps:
  *   raw    : i                                          (row-local position)
@@ -28,16 +29,26 @@
  *   - All array pointers are device memory owned by the caller.  The library
  *     allocates nothing on the device and never synchronises the host; work
  *     is enqueued on `stream` (a hipStream_t; NULL = the default stream).
- *   - Arguments are validated on the host before any HIP call; a rejected
- *     call enqueues nothing.  Device-side preconditions are not checked:
- *     page ids must be >= 0 with page_id * page_size + page_size - 1 < 2^31,
- *     and ragged rows must lie inside the packed buffer.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     rejected call enqueues nothing.  Device-side preconditions are not
+ *     checked: page ids must be >= 0 with page_id * page_size + page_size - 1
+ *     < 2^31, and ragged rows must lie inside the packed buffer.
  *   - Only gfx950 devices are supported; others return ETS_ERR_DEVICE.
  *   - `workspace` is caller-owned device memory of at least the size that
  *     ets_workspace_size() reports for the same (B, max row length, k) on the
- *     current device (0 bytes is valid; then workspace may be NULL).  It must
- *     not be shared by calls that may run concurrently.  Its contents between
- *     calls are irrelevant: every call initialises what it uses on `stream`.
+ *     current device (0 bytes is valid; then workspace may be NULL).  It is
+ *     used when the batch is too small to fill the device and each row is
+ *     split over several workgroups that exchange per-row histograms and
+ *     counters through it (sglang PR #37591 digest, the topk.hip excerpt:
+ *     the caller's allocator provides the row-split workspace).  It must be
+ *     zero-filled before its first use (ets_workspace_init, or any zero fill)
+ *     and every call returns the counters and tables it relies on to zero
+ *     (other words may keep stale data), so one workspace serves any number
+ *     of calls, including replays of a captured graph.  It must not be
+ *     shared by calls that may run concurrently.  The 32-bit word at byte
+ *     offset 128 is set non-zero if a call stopped waiting for the other
+ *     workgroups of a row (only possible when other work keeps the device
+ *     full for a very long time); that call's output is then undefined.
  */
 #ifndef ETS_TOPK_H
 #define ETS_TOPK_H
@@ -103,8 +114,7 @@ ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, in
  *   max_len_hint an upper bound of every lengths[b] (the host cannot read
  *                device lengths without a sync); it only steers the launch
  *                shape and the workspace size.  A row longer than the hint
- *                is still handled exactly when workspace is large enough for
- *                the longer length.
+ *                is still handled exactly, only more slowly.
  *   out          int32 [B, out_stride]: row_starts[b] + i per selected i.
  */
 ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,
@@ -115,17 +125,27 @@ ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,
 /*
  * Workspace bytes needed by a call with this batch size, longest row and k on
  * `device` (-1 = the current device).  Writes 0 when the call needs none.
+ * The size depends only on B once a workspace is needed at all.
  */
 ets_status ets_workspace_size(int32_t B, int64_t max_row_len, int32_t k, int32_t device,
                               size_t* bytes);
 
 /*
- * Blocks per row the library uses for (B, max_row_len) on a device with
- * `cu_count` compute units; 0 means one block per row.  Pure host function.
+ * Zero-fills `bytes` bytes of `workspace` on `stream` (one small kernel), as
+ * needed once before a workspace's first use.  workspace must be 16-byte
+ * aligned; bytes = 0 is a no-op.
+ */
+ets_status ets_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/*
+ * Workgroups per row the library uses for (B, max_row_len) on a device with
+ * `cu_count` compute units; 0 means one workgroup per row.  Pure host
+ * function.  Rows that fit one workgroup's 32768-score tile stay whole;
+ * longer rows are cut into chunks of about 8192 scores, at most 64 per row.
  * The environment variable ETS_ROW_SPLIT, when set to an integer >= 0,
- * overrides the heuristic (0 forces one block per row).  After the pages'
- * row_split heuristic (PR #37591 digest, the topk.hip excerpt), with
- * constants of this library.
+ * overrides the heuristic (0 or 1: one workgroup per row; n: n workgroups per
+ * row, at most 64).  After the pages' row_split heuristic (PR #37591 digest,
+ * the topk.hip excerpt), with constants of this library measured on MI355X.
  */
 int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count);
 

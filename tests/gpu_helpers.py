@@ -16,6 +16,23 @@ def dev():
     return torch.device("cuda:0")
 
 
+# Workspace layout of the row-group path (u32 words): a 64-word header, then
+# per row a 64-word record, three 4096-bin tables and a 4096-entry u64 tie list.
+WS_HDR = 64
+WS_ROW = 64 + 3 * 4096 + 2 * 4096
+WS_KEPT_ZERO = 64 + 3 * 4096   # record + tables: back at zero after every call
+
+
+def workspace_dirty(ws: torch.Tensor) -> int:
+    """Non-zero words among the header, records and tables of a workspace."""
+    torch.cuda.synchronize()
+    w = ws.view(torch.int32)
+    B = (w.numel() - WS_HDR) // WS_ROW
+    assert WS_HDR + B * WS_ROW == w.numel(), "not a row-group workspace"
+    rows = w[WS_HDR:].view(B, WS_ROW)[:, :WS_KEPT_ZERO]
+    return int(torch.count_nonzero(w[:WS_HDR]).item() + torch.count_nonzero(rows).item())
+
+
 def run_gpu(w, out_fill: int = POISON, scores=None):
     """Run workload ``w`` on the GPU; returns the int32 [B, k] output (numpy)."""
     d = dev()

@@ -28,7 +28,7 @@ def lib():
 
 def test_header_declares_the_api():
     assert {"ets_topk_raw", "ets_topk_paged", "ets_topk_ragged", "ets_workspace_size",
-            "ets_row_split", "ets_status_string"} <= set(_declared())
+            "ets_workspace_init", "ets_row_split", "ets_status_string"} <= set(_declared())
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -84,49 +84,44 @@ def test_workspace_query_validation(lib):
     assert lib.ets_workspace_size(4, 1000, 8, -1, None) == 1
 
 
+def test_workspace_init_validation(lib):
+    # zero bytes is a no-op; a null or misaligned pointer is rejected on the host
+    assert lib.ets_workspace_init(None, 0, None) == 0
+    assert lib.ets_workspace_init(None, 256, None) == 1
+    assert lib.ets_workspace_init(ctypes.c_void_p(0x1004), 256, None) == 1
+
+
 def test_row_split_env_override(tmp_path):
     code = ("import exact_top_selection_amd as e; "
             "print(e.row_split(4, 262144, 256), e.row_split(64, 32768, 256))")
-    env = dict(os.environ, ETS_ROW_SPLIT="7", PYTHONPATH=ROOT)
-    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
-                         check=True).stdout.split()
-    assert out == ["7", "7"]
-    env["ETS_ROW_SPLIT"] = "0"
-    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
-                         check=True).stdout.split()
-    assert out == ["0", "0"]
+
+    def run(v):
+        env = dict(os.environ, ETS_ROW_SPLIT=v, PYTHONPATH=ROOT)
+        return subprocess.run([sys.executable, "-c", code], env=env, capture_output=True,
+                              text=True, check=True).stdout.split()
+
+    assert run("7") == ["7", "7"]
+    assert run("0") == ["0", "0"]
+    assert run("1") == ["0", "0"]
+    assert run("1000") == ["64", "64"]
 
 
-def test_row_split_heuristic_and_workspace(lib):
+def test_row_split_heuristic():
     import exact_top_selection_amd as ets
     env = os.environ.pop("ETS_ROW_SPLIT", None)
     try:
-        # rows that fit one resident workgroup tile stay whole
-        assert ets.row_split(64, 32768, 256) == 0
-        assert ets.row_split(1, 2048, 256) == 0
-        # longer rows are cut into 4096-score chunks
-        assert ets.row_split(4, 32769, 256) == 9
-        assert ets.row_split(4, 262144, 256) == 64
-        assert ets.workspace_size(64, 32768, 1024) == 0
-        n = ets.workspace_size(4, 262144, 2048)
-        words = 4 * (16 + 4 * 64 + 4096 + 2 * 128)
-        assert n == (words * 4 + 255) // 256 * 256
+        # rows that fit one 32768-score workgroup tile stay whole, whatever the batch
+        for B, L in ((64, 32768), (128, 32768), (48, 8192), (1, 2048), (4, 4096), (1024, 8192)):
+            assert ets.row_split(B, L, 256) == 0, (B, L)
+        # longer rows are cut into chunks of about 8192 scores, at most 64
+        assert ets.row_split(4, 32769, 256) == 5
+        assert ets.row_split(4, 65536, 256) == 8
+        assert ets.row_split(2, 100000, 256) == 13
+        assert ets.row_split(4, 262144, 256) == 32
+        assert ets.row_split(4096, 262144, 256) == 32
+        assert ets.row_split(1, 10 ** 7, 256) == 64
+        assert ets.row_split(0, 262144, 256) == 0
+        assert ets.row_split(4, 262144, 0) == 32
     finally:
         if env is not None:
-            os.environ["ETS_ROW_SPLIT"] = env
-
-
-def test_split_call_rejects_small_workspace(lib):
-    import ctypes as C
-    env = os.environ.get("ETS_ROW_SPLIT")
-    os.environ["ETS_ROW_SPLIT"] = "4"
-    try:
-        fake = C.c_void_p(0x1000)
-        # a split call without its workspace is rejected before any HIP call
-        st = lib.ets_topk_raw(fake, 65536, 2, 65536, None, 8, fake, 8, None, 0, None)
-        assert st == 3
-    finally:
-        if env is None:
-            os.environ.pop("ETS_ROW_SPLIT", None)
-        else:
             os.environ["ETS_ROW_SPLIT"] = env

@@ -1,17 +1,22 @@
-"""GPU parity of the row-split path (several workgroups per row).
+"""GPU parity of the row-group path (several workgroups per row, one launch).
 
-The path is forced with ETS_ROW_SPLIT (read by the library at every call);
-its results must equal the oracle's and the one-workgroup path's.
+The path is chosen by the library's heuristic or forced with ETS_ROW_SPLIT
+(read at every call); its results must equal the oracle's and the
+one-workgroup path's.  The workspace's counters and tables must come back
+zero after every call.
 """
 import contextlib
+import ctypes
 import os
 
 import numpy as np
 import pytest
+import torch
 
+import exact_top_selection_amd as ets
 import workloads
 from workloads import Workload
-from tests.gpu_helpers import assert_parity, run_gpu, run_oracle
+from tests.gpu_helpers import WS_HDR, WS_ROW, assert_parity, dev, run_gpu, run_oracle, workspace_dirty
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +39,20 @@ def _raw(name, x, k, lens=None):
     return Workload(name, "raw", k, B, x, L=L, lens=None if lens is None else lens.astype(np.int32))
 
 
-@pytest.mark.parametrize("g", [2, 3, 8, 17])
+def _assert_clean(ws):
+    """The error word is zero, and so are the counters and histogram tables a
+    call relies on; the tie lists behind them may keep stale entries."""
+    torch.cuda.synchronize()
+    assert ets.workspace_error(ws) == 0, "a call stopped waiting for its row group"
+    nz = workspace_dirty(ws)
+    assert nz == 0, "%d counter or table words left non-zero" % nz
+
+
+def _cached_workspaces():
+    return [w for w in ets._ws_cache.values()]
+
+
+@pytest.mark.parametrize("g", [2, 3, 8, 17, 64])
 @pytest.mark.parametrize("name", ["C2", "C3"])
 def test_forced_split_matches_single(name, g):
     w = workloads.make(name, seed=45)
@@ -42,6 +60,7 @@ def test_forced_split_matches_single(name, g):
     w.scores = np.ascontiguousarray(w.scores[:16])
     w.lens = w.lens[:16]
     w.page_table = w.page_table[:16]
+    print("case", name, "G", g, flush=True)
     with split(0):
         single = run_gpu(w)
     with split(g):
@@ -49,17 +68,24 @@ def test_forced_split_matches_single(name, g):
     want = run_oracle(w)
     assert_parity(w, single, want)
     assert_parity(w, got, want)
+    for ws in _cached_workspaces():
+        _assert_clean(ws)
 
 
-@pytest.mark.parametrize("g", [4, 16])
+@pytest.mark.parametrize("g", [2, 4, 16])
 def test_forced_split_concentrated(g):
+    """88% of a row in one 12-bit bucket: the tie list overflows and the group
+    narrows the bucket by further rounds, down to positions among equal keys."""
     rng = np.random.Generator(np.random.PCG64(11))
     x = np.stack([workloads.concentrated_row(rng, 32768) for _ in range(4)])
     lens = np.array([32768, 20000, 4097, 2050], dtype=np.int32)
-    for k in (1024, 2048):
+    for k in (1, 1024, 2048):
         w = _raw("conc-split", x, k, lens)
+        print("case concentrated G", g, "k", k, flush=True)
         with split(g):
             assert_parity(w, run_gpu(w), run_oracle(w))
+    for ws in _cached_workspaces():
+        _assert_clean(ws)
 
 
 def test_split_long_rows_default_heuristic():
@@ -81,6 +107,38 @@ def test_split_all_equal_and_ties():
         assert_parity(w, run_gpu(w), run_oracle(w))
 
 
+@pytest.mark.parametrize("g", [2, 8])
+def test_split_special_values(g):
+    """Signed zeros, subnormals, infinities and NaNs ranked by key in the group path."""
+    rng = np.random.default_rng(77)
+    L = 16384
+    bits = rng.integers(0, 2 ** 32, size=(4, L), dtype=np.uint64).astype(np.uint32)
+    specials = np.array([0x00000000, 0x80000000, 0x00000001, 0x807FFFFF, 0x7F800000, 0xFF800000,
+                         0x7FC00000, 0xFFC00000, 0x3F800000], dtype=np.uint32)
+    bits[1] = specials[rng.integers(0, specials.size, size=L)]
+    bits[2, :] = 0x80000000          # all -0.0 ...
+    bits[2, ::97] = 0x00000000       # ... with some +0.0 above them
+    bits[3] = rng.integers(1, 1 << 23, size=L).astype(np.uint32)  # positive subnormals
+    x = bits.view(np.float32)
+    for k in (1, 1000, 2048):
+        w = _raw("special-split", x, k)
+        with split(g):
+            assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+def test_split_short_rows_and_empty_chunks():
+    """Rows at and just above k, where most chunks of a 17-way split are empty."""
+    rng = np.random.default_rng(5)
+    k = 1024
+    L = 8192
+    lens = np.array([0, 1, k - 1, k, k + 1, k + 3, 2 * k, 4100, L], dtype=np.int32)
+    x = rng.standard_normal((lens.size, L)).astype(np.float32)
+    w = _raw("short-split", x, k, lens)
+    for g in (2, 17, 64):
+        with split(g):
+            assert_parity(w, run_gpu(w), run_oracle(w))
+
+
 def test_split_concentrated_long_rows():
     rng = np.random.Generator(np.random.PCG64(12))
     x = np.stack([workloads.concentrated_row(rng, 65536) for _ in range(2)])
@@ -98,11 +156,22 @@ def test_split_paged_long_rows():
     assert_parity(w, run_gpu(w), run_oracle(w))
 
 
+def test_split_paged_odd_page_size():
+    """A page size that is not a power of two reads page ids from global memory."""
+    rng = np.random.default_rng(32)
+    B, L, ps, k = 6, 12000, 48, 1024
+    npg = (L + ps - 1) // ps
+    x = rng.standard_normal((B, L)).astype(np.float32)
+    lens = rng.integers(1000, L + 1, size=B).astype(np.int32)
+    pt = np.stack([rng.permutation(npg) for _ in range(B)]).astype(np.int32)
+    w = Workload("paged-odd", "paged", k, B, x, L=L, lens=lens, page_table=pt, page_size=ps)
+    for g in (3, 8):
+        with split(g):
+            assert_parity(w, run_gpu(w), run_oracle(w))
+
+
 def test_ragged_row_longer_than_hint():
-    """The last chunk of a row runs to the row's end, whatever the hint said."""
-    import torch
-    import exact_top_selection_amd as ets
-    from tests.gpu_helpers import dev
+    """A chunk longer than one tile (the row outgrew the hint) is streamed."""
     rng = np.random.default_rng(41)
     lengths = np.array([50000, 90000, 3000, 1024], dtype=np.int32)
     starts = np.zeros_like(lengths)
@@ -115,3 +184,66 @@ def test_ragged_row_longer_than_hint():
                               torch.from_numpy(lengths).to(d), 2048, max_len=hint)
         torch.cuda.synchronize()
         assert_parity(w, out.cpu().numpy(), run_oracle(w))
+
+
+def test_one_workspace_across_shapes_and_apis():
+    """Every call returns its workspace's counters and tables to zero, so one
+    buffer serves calls of any shape and map in turn."""
+    d = dev()
+    ws = ets.new_workspace(128, 262144, 2048, d)  # the largest batch below
+    _assert_clean(ws)
+    cases = [workloads.make(n, seed=60 + i) for i, n in enumerate(["C3", "C5", "C2", "C4", "C3"])]
+    for w in cases:
+        s = torch.from_numpy(w.scores).to(d)
+        out = torch.full((w.B, w.k), 3, dtype=torch.int32, device=d)
+        if w.api == "paged":
+            ets.topk_paged(s, torch.from_numpy(w.lens).to(d), torch.from_numpy(w.page_table).to(d),
+                           out, w.page_size, workspace=ws)
+        elif w.api == "raw":
+            ets.topk_raw(s, w.k, None if w.lens is None else torch.from_numpy(w.lens).to(d),
+                         out=out, workspace=ws)
+        else:
+            ets.topk_ragged(s, torch.from_numpy(w.row_starts).to(d),
+                            torch.from_numpy(w.lengths).to(d), w.k, max_len=w.max_len, out=out,
+                            workspace=ws)
+        print("case", w.name, flush=True)
+        _assert_clean(ws)
+        assert_parity(w, out.cpu().numpy(), run_oracle(w))
+
+
+def test_workspace_init_zero_fills():
+    d = dev()
+    ws = torch.full((4 * (WS_HDR + 2 * WS_ROW),), 0xAB, dtype=torch.uint8, device=d)
+    ets.workspace_init(ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws).item() == 0
+
+
+def test_split_call_rejects_small_workspace():
+    lib = ets._load()
+    d = dev()
+    B, L, k = 4, 65536, 64
+    need = ets.workspace_size(B, L, k)
+    assert need > 0
+    x = torch.zeros((B, L), dtype=torch.float32, device=d)
+    out = torch.empty((B, k), dtype=torch.int32, device=d)
+    ws = torch.zeros(need, dtype=torch.uint8, device=d)
+    st = torch.cuda.current_stream().cuda_stream
+    args = (x.data_ptr(), L, B, L, None, k, out.data_ptr(), k)
+    assert lib.ets_topk_raw(*args, ws.data_ptr(), need - 1, st) == 3
+    assert lib.ets_topk_raw(*args, None, 0, st) == 3
+    assert lib.ets_topk_raw(*args, ws.data_ptr() + 4, need - 4, st) == 3  # misaligned
+    assert lib.ets_topk_raw(*args, ws.data_ptr(), need, st) == 0
+    _assert_clean(ws)
+
+
+def test_workspace_size_formula():
+    # header + per-row record, three 4096-bin tables and the 4096-entry tie list
+    env = os.environ.pop("ETS_ROW_SPLIT", None)
+    try:
+        for B in (1, 4, 64):
+            assert ets.workspace_size(B, 262144, 2048) == 4 * (WS_HDR + B * WS_ROW)
+        assert ets.workspace_size(4096, 4096, 1024) == 0
+    finally:
+        if env is not None:
+            os.environ["ETS_ROW_SPLIT"] = env
