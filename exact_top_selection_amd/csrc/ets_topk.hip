@@ -103,6 +103,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
+// Slot masks: mask = 2 * mask + (a < b), resp. (a <= b), as one compare into
+// VCC and one add with carry-in (the compiler's form takes a select and a
+// shifted add on top of the compare).
+__device__ __forceinline__ uint32_t shift_in_lt(uint32_t mask, uint32_t a, uint32_t b) {
+  asm("v_cmp_lt_u32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc" : "+v"(mask) : "v"(a), "v"(b) : "vcc");
+  return mask;
+}
+__device__ __forceinline__ uint32_t shift_in_le(uint32_t mask, uint32_t a, uint32_t b) {
+  asm("v_cmp_le_u32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc" : "+v"(mask) : "v"(a), "v"(b) : "vcc");
+  return mask;
+}
+
 struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
 struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
 struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
@@ -353,12 +365,14 @@ __device__ __forceinline__ void hist_clear(uint32_t* hist) {
 // above any range.  Round r counts into hist[r & 1] and clears the other
 // buffer.  Precondition: hist[round & 1] is zero and a barrier has passed.
 // Each wave probes (with probe_key) whether its lanes pile into one bin and
-// only then merges its LDS atomics.  Returns the refined state.
+// only then merges its LDS atomics.  Precondition: no key that for_each
+// visits lies above in.hi.  Returns the refined state.
 template <int T, class ForEach>
 __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel in, uint32_t nm1,
                                       uint32_t n_pad, uint32_t probe_key, int& round) {
   uint32_t lo = in.lo, hi = in.hi, kk = in.kk, bucket = in.bucket;
   uint32_t tie = 0, dlo = 0, dhi = nm1;
+  const int first_round = round;
   while (bucket > static_cast<uint32_t>(kSmallCap) && lo != hi && round < kMaxRounds) {
     uint32_t* hist = sm.hist[round & 1];
     hist_clear<T>(sm.hist[(round + 1) & 1]);
@@ -376,6 +390,14 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
       for_each([&](uint32_t x, int32_t, int) {
         const uint32_t d = x - rlo;
         hist_add_peel(hist, d <= span, d >> s);
+      });
+    } else if (round == first_round && rlo != 0 && ((0u - rlo) >> s) >= kHistBins + 64) {
+      // First round: nothing lies above hi, and a key under lo wraps to a
+      // difference whose bin lies past every lane's dummy, so a min picks the
+      // dummy without a range test (in-range bins are the same as below).
+      const uint32_t dummy = kHistBins + __lane_id();
+      for_each([&](uint32_t x, int32_t, int) {
+        atomicAdd(&hist[min((x - rlo) >> s, dummy)], 1u);
       });
     } else {
       const uint32_t dummy = kHistBins + __lane_id();
@@ -681,8 +703,8 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
       const uint32_t khi = sel.hi, klo = sel.lo, kspan = sel.hi - sel.lo;
       if (klo != 0) {
         for_each([&](uint32_t x, int32_t, int) {
-          wmask = wmask + wmask + (x > khi ? 1u : 0u);
-          cmask = cmask + cmask + (x - klo <= kspan ? 1u : 0u);
+          wmask = shift_in_lt(wmask, khi, x);
+          cmask = shift_in_le(cmask, x - klo, kspan);
         });
       } else {
         for_each([&](uint32_t x, int32_t pos, int) {
