@@ -504,9 +504,11 @@ __device__ __forceinline__ void rank_bucket(const uint2* cand, uint32_t nc, uint
   constexpr int G = T / kSmallCap;
   static_assert(G == 2 || G == 4 || G == 8, "2, 4 or 8 lanes per bucket entry");
   constexpr int Q = kSmallCap / G;  // entries compared by each lane
-  constexpr int QB = 16;            // entries read per batch
+  constexpr int QB = 4;             // entries read per batch: small buckets read little
   const uint32_t i = threadIdx.x / G;
   const uint32_t part = threadIdx.x % G;
+  // a wave whose entries all lie past the bucket has nothing to rank
+  if ((threadIdx.x & ~63u) / G >= nc) return;
   const uint32_t last = nc > 0 ? nc - 1 : 0;
   const uint2 ci = cand[min(i, last)];
   const uint64_t vi = (static_cast<uint64_t>(ci.x) << 32) | static_cast<uint32_t>(~ci.y);
@@ -646,10 +648,13 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
     }
     __syncthreads();
     uint32_t gmax = 0, gb = 0xFFFFFFFFu;
+    static_assert(W % 4 == 0, "per-wave partials are read four at a time");
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      gmax = max(gmax, sm.red[w]);
-      gb = min(gb, sm.red[16 + w]);
+    for (int w = 0; w < W; w += 4) {
+      const uint4 a = *reinterpret_cast<const uint4*>(&sm.red[w]);
+      const uint4 c = *reinterpret_cast<const uint4*>(&sm.red[16 + w]);
+      gmax = max(gmax, max(max(a.x, a.y), max(a.z, a.w)));
+      gb = min(gb, min(min(c.x, c.y), min(c.z, c.w)));
     }
     sel0.hi = gmax;
     if (nfull * jth >= k) {
