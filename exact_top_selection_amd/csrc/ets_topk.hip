@@ -845,7 +845,8 @@ constexpr int kHdrWords = 64;
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 enum HdrField : int { kHdrTicket = 0, kHdrFinished = 16, kHdrError = 32 };
-enum GroupRecField : int { kRecBarrier = 0, kRecDone = 16, kRecCursor = 32 /* u64 */, kRecTouched = 48 };
+enum GroupRecField : int { kRecBarrier = 0, kRecDone = 16, kRecCursor = 32 /* u64 */, kRecTouched = 48,
+                          kRecLb = 56, kRecHi = 60 };
 
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1023,19 +1024,77 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   const uint32_t pad = span.pad_slots();
   const int32_t nc = span.end - span.start;
 
-  // ---- round 0: top 12 key bits
+  // ---- bounds of the row, in one exchange: its largest key, and a lower
+  // bound of its k-th largest.  A chunk whose lanes' jth-largest keys are at
+  // least k distinct scores bounds the row's k-th largest by their minimum
+  // (jth = ceil(k / lanes holding scores) <= 2); other chunks offer 0.
   {
-    const uint32_t probe = RES ? key[0] >> 20 : 0u;
-    const bool peel = __popcll(__ballot(probe == readfirstlane(probe))) > kPeelShare;
-    if (peel) {
-      for_each([&](uint32_t x, int32_t, int) { hist_add_peel(lh, true, x >> 20); });
-    } else {
-      for_each([&](uint32_t x, int32_t, int) { atomicAdd(&lh[x >> 20], 1u); });
+    uint32_t m1 = 0, m2 = 0;
+    for_each([&](uint32_t x, int32_t, int) {
+      m2 = max(m2, min(m1, x));
+      m1 = max(m1, x);
+    });
+    const int32_t holders = V4 ? min(T, (nc + 3) / 4) : min(T, nc);
+    const int32_t jth = holders > 0 ? (k + holders - 1) / holders : 3;
+    const int32_t jpos = V4 ? 4 * tid + jth - 1 : (jth - 1) * T + tid;
+    const bool full = jth <= 2 && span.start + jpos < span.end;
+    const int32_t nfull = jth > 2 ? 0 : (V4 ? min(T, max(0, (nc - jth) / 4 + 1)) : min(T, max(0, nc - (jth - 1) * T)));
+    const uint32_t vmax = wave_reduce(m1, OpMax());
+    const uint32_t vlb = wave_reduce(full ? (jth == 1 ? m1 : m2) : 0xFFFFFFFFu, OpMin());
+    if (__lane_id() == 0) {
+      sm.sel.wsum[wid] = vmax;
+      sm.wsum2[wid] = vlb;
     }
     __syncthreads();
-    if (tid == 0) lh[0] -= pad;  // padding slots hold key 0
+    if (tid == 0) {
+      uint32_t cmax = 0, clb = 0xFFFFFFFFu;
+      for (int w = 0; w < W; ++w) {
+        cmax = max(cmax, sm.sel.wsum[w]);
+        clb = min(clb, sm.wsum2[w]);
+      }
+      if (nc > 0) max_dev(rec + kRecHi, cmax);
+      if (nfull * jth >= k) max_dev(rec + kRecLb, clb);
+    }
+  }
+  group_sync(rec + kRecBarrier, static_cast<uint32_t>(G), err);
+  uint32_t nbar = 1;  // group barriers passed
+  Sel sel{};
+  sel.lo = ld_dev(rec + kRecLb);
+  sel.hi = ld_dev(rec + kRecHi);
+  sel.kk = static_cast<uint32_t>(k);
+  sel.dlo = 0u;
+  sel.dhi = nm1;
+
+  // ---- round 0: a 12-bit histogram of [lo, hi]
+  int s0;
+  {
+    const uint32_t lo = sel.lo, span_k = sel.hi - sel.lo;
+    s0 = digit_shift(span_k);
+    const int s = s0;
+    const uint32_t pd = (RES ? key[0] : 0u) - lo;
+    const uint32_t pbin = pd >> s;
+    const bool peel = __popcll(__ballot(pd <= span_k && pbin == readfirstlane(pbin))) > kPeelShare;
+    const uint32_t dummy = kHistBins + __lane_id();
+    if (peel) {
+      for_each([&](uint32_t x, int32_t, int) {
+        const uint32_t d = x - lo;
+        hist_add_peel(lh, d <= span_k, d >> s);
+      });
+    } else if (lo != 0 && ((0u - lo) >> s) >= kHistBins + 64) {
+      // nothing lies above hi, and a key under lo wraps past every dummy
+      for_each([&](uint32_t x, int32_t, int) { atomicAdd(&lh[min((x - lo) >> s, dummy)], 1u); });
+    } else {
+      for_each([&](uint32_t x, int32_t, int) {
+        const uint32_t d = x - lo;
+        atomicAdd(&lh[d <= span_k ? d >> s : dummy], 1u);
+      });
+    }
+    if (tid == 0) sm.sel.res[0] = 0;  // no threshold in the chunk: push every bin
+    __syncthreads();
+    if (lo == 0 && tid == 0) lh[0] -= pad;  // padding slots hold key 0
     __syncthreads();
   }
+  // this chunk's threshold bin: nothing below it can hold the row's threshold
   uint32_t from = kHistBins;
   if (nc > 0) {
     find_threshold_bin<T>(lh, static_cast<uint32_t>(min(k, nc)), 0u, sm.sel.wsum, sm.sel.res);
@@ -1043,15 +1102,9 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   }
   if (tid == 0 && from < static_cast<uint32_t>(kHistBins)) max_dev(rec + kRecTouched, kHistBins - from);
   push_bins<T>(lh, from, ghist);
-  group_sync(rec + kRecBarrier, static_cast<uint32_t>(G), err);
-  Sel sel{};
-  sel.lo = 0u;
-  sel.hi = 0xFFFFFFFFu;
-  sel.kk = static_cast<uint32_t>(k);
-  sel.dlo = 0u;
-  sel.dhi = nm1;
+  group_sync(rec + kRecBarrier, static_cast<uint32_t>(G) * ++nbar, err);
   read_bins<T>(ghist, sel.kk, sm.sel);
-  narrow(sel, sm.sel.res, 32 - kHistBits);
+  narrow(sel, sm.sel.res, s0);
 
   // ---- further rounds while the bucket exceeds the tie list
   int round = 1;
@@ -1090,7 +1143,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     }
     __syncthreads();
     push_bins<T>(lh, 0u, buf);
-    group_sync(rec + kRecBarrier, static_cast<uint32_t>(G) * (round + 1), err);
+    group_sync(rec + kRecBarrier, static_cast<uint32_t>(G) * ++nbar, err);
     if (g == 0) {
       // the previous round's table is read by every member by now and is next
       // used two rounds on, after this member's next arrival
@@ -1256,6 +1309,8 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     st_dev(rec + kRecDone, 0u);
     st_dev(reinterpret_cast<uint64_t*>(rec + kRecCursor), 0ull);
     st_dev(rec + kRecTouched, 0u);
+    st_dev(rec + kRecLb, 0u);
+    st_dev(rec + kRecHi, 0u);
   }
 }
 
