@@ -134,8 +134,8 @@ def traffic_report(d: str, workload: str, seed: int) -> int:
             raise SystemExit("no counter csv under %s/%s" % (d, sub))
         return _pmc_per_dispatch(files[0], counter, part)
 
-    kf, nkf = one("fetch", "FETCH_SIZE", "row_topk_kernel")
-    kw, nkw = one("write", "WRITE_SIZE", "row_topk_kernel")
+    kf, nkf = one("fetch", "FETCH_SIZE", "topk_kernel")
+    kw, nkw = one("write", "WRITE_SIZE", "topk_kernel")
     cf, ncf = one("copy_fetch", "FETCH_SIZE", "copy")
     cw, ncw = one("copy_write", "WRITE_SIZE", "copy")
     # counters are in KiB per dispatch; scale each by the copy kernel's reading
@@ -265,6 +265,10 @@ def main() -> int:
     abytes = algorithmic_bytes(w)
     achieved = abytes / (ms_per_step * 1e-3) / 1e9  # GB/s; one kernel launch per step
 
+    # the one kernel a step launches: one workgroup per row, or row groups
+    split = ets.row_split(w.B, w.max_len if w.api == "ragged" else w.L,
+                          torch.cuda.get_device_properties(dev).multi_processor_count)
+    kernel = "group_topk_kernel (%d workgroups per row)" % split if split else "row_topk_kernel"
     result = {
         "metric": METRIC,
         "value": rows_per_s,
@@ -293,7 +297,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(w.name),
-            "kernel": "row_topk_kernel",
+            "kernel": kernel,
             "kernel_us_per_launch": ms_per_step * 1e3,
         },
     }
