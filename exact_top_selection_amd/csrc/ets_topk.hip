@@ -1170,10 +1170,19 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   uint32_t wmask = 0, cmask = 0;  // RES: bit PT-1-j marks slot j
   if constexpr (RES) {
     static_assert(PT <= 32, "slot masks are 32 bits");
-    for_each([&](uint32_t x, int32_t pos, int) {
-      wmask = wmask + wmask + (sel_winner(sel, nm1, cend, x, pos) ? 1u : 0u);
-      cmask = cmask + cmask + (sel_bucket(sel, nm1, cend, x, pos) ? 1u : 0u);
-    });
+    if (!sel.tie && sel.lo != 0) {
+      // padding (key 0) lies below lo: the plain range tests hold
+      const uint32_t khi = sel.hi, klo = sel.lo, kspan = sel.hi - sel.lo;
+      for_each([&](uint32_t x, int32_t, int) {
+        wmask = shift_in_lt(wmask, khi, x);
+        cmask = shift_in_le(cmask, x - klo, kspan);
+      });
+    } else {
+      for_each([&](uint32_t x, int32_t pos, int) {
+        wmask = wmask + wmask + (sel_winner(sel, nm1, cend, x, pos) ? 1u : 0u);
+        cmask = cmask + cmask + (sel_bucket(sel, nm1, cend, x, pos) ? 1u : 0u);
+      });
+    }
     nw = static_cast<uint32_t>(__popc(wmask));
     nb = static_cast<uint32_t>(__popc(cmask));
   } else {
