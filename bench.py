@@ -161,6 +161,39 @@ def traffic_report(d: str, workload: str, seed: int) -> int:
     return 0
 
 
+
+def timed(torch, step, steps: int, warmup: int, eager: bool) -> float:
+    """Milliseconds for exactly `steps` calls of step(i), after `warmup` untimed
+    ones; the timed calls are one captured graph unless `eager`.  HIP events on
+    the stream the calls run on."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if not eager:
+        graph = torch.cuda.CUDAGraph()
+        cap_stream = torch.cuda.Stream()
+        cap_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap_stream):
+            with torch.cuda.graph(graph, stream=cap_stream):
+                for i in range(steps):
+                    step(warmup + i)
+        torch.cuda.current_stream().wait_stream(cap_stream)
+        torch.cuda.synchronize()
+        graph.replay()  # uploads the graph; untimed
+        torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if eager:
+        for i in range(steps):
+            step(warmup + i)
+    else:
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop)
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +203,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-floors", action="store_true",
+                    help="skip the empty-launch and read-only floors")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -230,36 +265,7 @@ def main() -> int:
             ets.topk_ragged(ring[i % R], starts, lengths, w.k, max_len=max_len, out=out,
                             workspace=ws)
 
-    # ---- warmup (eager), then capture the K timed steps into one graph
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        cap_stream = torch.cuda.Stream()
-        cap_stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap_stream):
-            with torch.cuda.graph(graph, stream=cap_stream):
-                for i in range(args.steps):
-                    step(args.warmup + i)
-        torch.cuda.current_stream().wait_stream(cap_stream)
-        torch.cuda.synchronize()
-        graph.replay()  # uploads the graph; untimed
-        torch.cuda.synchronize()
-
-    # ---- timed region: exactly K steps
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    if args.eager:
-        for i in range(args.steps):
-            step(args.warmup + i)
-    else:
-        graph.replay()
-    stop.record()
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
+    ms_total = timed(torch, step, args.steps, args.warmup, args.eager)
     ms_per_step = ms_total / args.steps
     rows_per_s = w.B / (ms_per_step * 1e-3)
     abytes = algorithmic_bytes(w)
@@ -301,6 +307,28 @@ def main() -> int:
             "kernel_us_per_launch": ms_per_step * 1e3,
         },
     }
+    if not args.no_floors:
+        # the same grid with empty workgroups, and the same reads with nothing
+        # selected, timed the same way over the same input ring
+        max_len = w.max_len if w.api == "ragged" else w.L
+        sink = torch.empty(w.B * max(1, split), dtype=torch.int32, device=dev)
+        if w.api == "ragged":
+            def read_step(i):
+                ets.floor_read(ring[i % R], lengths, starts, max_len, sink=sink)
+        else:
+            def read_step(i):
+                ets.floor_read(ring[i % R], lens, sink=sink)
+
+        def launch_step(i):
+            ets.floor_launch(w.B, max_len, dev)
+        result["floors"] = {
+            "launch_us": timed(torch, launch_step, args.steps, args.warmup, args.eager)
+            * 1e3 / args.steps,
+            "read_us": timed(torch, read_step, args.steps, args.warmup, args.eager)
+            * 1e3 / args.steps,
+            "what": "per call: an empty launch of the same grid; the same grid reading "
+                    "the same bytes and forming keys, one max per workgroup",
+        }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

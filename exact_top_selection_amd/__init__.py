@@ -26,7 +26,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["topk_raw", "topk_paged", "topk_ragged", "workspace_size", "row_split",
+__all__ = ["topk_raw", "topk_paged", "topk_ragged", "workspace_size", "row_split", "floor_read",
+           "floor_launch",
            "new_workspace", "workspace_init", "workspace_error", "library_path", "MAX_K",
            "EtsError"]
 
@@ -67,8 +68,11 @@ def _load():
             lib.ets_row_split.argtypes = [i32, i64, i32]
             lib.ets_workspace_init.argtypes = [vp, sz, vp]
             lib.ets_status_string.argtypes = [i32]
+            lib.ets_floor_read.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp, i64, vp]
+            lib.ets_floor_launch.argtypes = [i32, i64, vp]
             for fn in (lib.ets_topk_raw, lib.ets_topk_paged, lib.ets_topk_ragged,
-                       lib.ets_workspace_size, lib.ets_row_split, lib.ets_workspace_init):
+                       lib.ets_workspace_size, lib.ets_row_split, lib.ets_workspace_init,
+                       lib.ets_floor_read, lib.ets_floor_launch):
                 fn.restype = ctypes.c_int32
             lib.ets_status_string.restype = ctypes.c_char_p
             _lib = lib
@@ -287,3 +291,54 @@ def topk_ragged(packed: torch.Tensor, row_starts: torch.Tensor, lengths: torch.T
                                      _stream(dev))
     _check(st, "ets_topk_ragged")
     return out
+
+
+def floor_read(scores: torch.Tensor, lens: Optional[torch.Tensor] = None,
+               row_starts: Optional[torch.Tensor] = None, max_len: Optional[int] = None,
+               sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Measurement floor: reads what a selection call on the same rows reads,
+    with its grid and loads, and returns each workgroup's largest key
+    (int32 view of uint32 words, one per workgroup).
+
+    Dense: ``scores`` [B, L] with optional ``lens``.  Ragged: ``scores`` is the
+    packed 1-D buffer, ``lens`` the lengths and ``row_starts`` the offsets;
+    ``max_len`` bounds the lengths.
+    """
+    dev = scores.device
+    if row_starts is None:
+        _require(scores, "scores", torch.float32, 2)
+        B, L = scores.shape
+        stride = _rows(scores, "scores")
+        if lens is not None:
+            _vec(lens, "lens", B)
+        max_len = L
+    else:
+        _require(scores, "scores", torch.float32, 1)
+        B = row_starts.shape[0]
+        _vec(row_starts, "row_starts", B)
+        if lens is None:
+            raise ValueError("ragged rows need lens")
+        _vec(lens, "lens", B)
+        if max_len is None:
+            raise ValueError("ragged rows need max_len")
+        L, stride = 0, 0
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    words = B * max(1, row_split(B, max_len, cu))
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=dev)
+    _require(sink, "sink", torch.int32, 1)
+    with torch.cuda.device(dev):
+        st = _load().ets_floor_read(scores.data_ptr(), stride, B, L,
+                                    lens.data_ptr() if lens is not None else None,
+                                    row_starts.data_ptr() if row_starts is not None else None,
+                                    max_len, sink.data_ptr(), sink.numel(), _stream(dev))
+    _check(st, "ets_floor_read")
+    return sink[:words]
+
+
+def floor_launch(B: int, max_row_len: int, device: Optional[torch.device] = None) -> None:
+    """Measurement floor: one empty launch of a selection call's grid."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    with torch.cuda.device(dev):
+        st = _load().ets_floor_launch(B, max_row_len, _stream(dev))
+    _check(st, "ets_floor_launch")

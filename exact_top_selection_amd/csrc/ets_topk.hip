@@ -839,14 +839,17 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // records and the tables to zero (tie lists may keep stale entries).
 
 constexpr int kTieCap = 4096;      // tie-list entries per row
+constexpr int kCoarseBits = 8;     // round 0 exchanges 2^kCoarseBits bins per row
+constexpr int kCoarseBins = 1 << kCoarseBits;
+constexpr int kFinePerCoarse = kHistBins / kCoarseBins;
 constexpr int kGroupPtCap = 1024;  // chunk page-table entries staged in LDS
 constexpr int kRecWords = 64;      // per-row record: its own 256-byte line
 constexpr int kHdrWords = 64;
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 enum HdrField : int { kHdrTicket = 0, kHdrFinished = 16, kHdrError = 32 };
-enum GroupRecField : int { kRecBarrier = 0, kRecDone = 16, kRecCursor = 32 /* u64 */, kRecTouched = 48,
-                          kRecLb = 56, kRecHi = 60 };
+enum GroupRecField : int { kRecBarrier = 0, kRecDone = 16, kRecCursor = 32 /* u64 */, kRecLb = 56,
+                          kRecHi = 60 };
 
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -940,8 +943,51 @@ __device__ __forceinline__ void read_bins(const uint32_t* src, uint32_t kk, SelS
 }
 
 template <int T>
-__device__ __forceinline__ void clear_bins(uint32_t* buf, uint32_t from) {
-  for (uint32_t i = from + threadIdx.x; i < static_cast<uint32_t>(kHistBins); i += T) st_dev(buf + i, 0u);
+__device__ __forceinline__ void clear_bins(uint32_t* buf, uint32_t count) {
+  for (uint32_t i = threadIdx.x; i < count; i += T) st_dev(buf + i, 0u);
+}
+
+// Adds the LDS histogram, merged kFinePerCoarse bins at a time, into the
+// coarse table dst (device atomics; zero bins are skipped) and clears it.
+template <int T>
+__device__ __forceinline__ void push_coarse(uint32_t* lh, uint32_t* dst) {
+  static_assert(kHistBins / T == 4 && kFinePerCoarse == 16, "a quad of lanes holds one coarse bin");
+  uint4* q = reinterpret_cast<uint4*>(lh) + threadIdx.x;
+  const uint4 c = *q;
+  *q = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t v = (c.x + c.y) + (c.z + c.w);
+  v += dpp_perm<0xB1>(v);  // quad_perm [1,0,3,2]
+  v += dpp_perm<0x4E>(v);  // quad_perm [2,3,0,1]
+  if ((threadIdx.x & 3u) == 0 && v != 0) add_dev(dst + (threadIdx.x >> 2), v);
+}
+
+// Every wave reads the coarse table src and finds its threshold bin for kk:
+// (bin, entries above it, entries in it), the same in every lane.  No barrier.
+__device__ __forceinline__ uint3 find_coarse(const uint32_t* src, uint32_t kk) {
+  static_assert(kCoarseBins == 4 * 64, "a lane holds four coarse bins");
+  const uint32_t l = __lane_id();
+  const uint64_t a = ld_dev(reinterpret_cast<const uint64_t*>(src + 4 * l));
+  const uint64_t b = ld_dev(reinterpret_cast<const uint64_t*>(src + 4 * l + 2));
+  const uint32_t h[4] = {static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32),
+                         static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32)};
+  const uint32_t sum = (h[0] + h[1]) + (h[2] + h[3]);
+  const uint32_t incl = wave_incl_scan(sum);
+  uint32_t above = readlane(incl, 63) - incl;  // entries in higher lanes' bins
+  uint32_t t = 0, ta = 0, th = 0;
+  bool hit = false;
+#pragma unroll
+  for (int i = 3; i >= 0; --i) {
+    if (!hit && above < kk && kk <= above + h[i]) {
+      hit = true;
+      t = 4 * l + i;
+      ta = above;
+      th = h[i];
+    }
+    above += h[i];
+  }
+  const uint64_t m = __ballot(hit);
+  const int src_lane = m ? __ffsll(static_cast<unsigned long long>(m)) - 1 : 0;
+  return make_uint3(readlane(t, src_lane), readlane(ta, src_lane), readlane(th, src_lane));
 }
 
 // Shift that maps a range of span + 1 values onto at most kHistBins bins.
@@ -1089,22 +1135,19 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
         atomicAdd(&lh[d <= span_k ? d >> s : dummy], 1u);
       });
     }
-    if (tid == 0) sm.sel.res[0] = 0;  // no threshold in the chunk: push every bin
     __syncthreads();
     if (lo == 0 && tid == 0) lh[0] -= pad;  // padding slots hold key 0
     __syncthreads();
   }
-  // this chunk's threshold bin: nothing below it can hold the row's threshold
-  uint32_t from = kHistBins;
-  if (nc > 0) {
-    find_threshold_bin<T>(lh, static_cast<uint32_t>(min(k, nc)), 0u, sm.sel.wsum, sm.sel.res);
-    from = sm.sel.res[0];
-  }
-  if (tid == 0 && from < static_cast<uint32_t>(kHistBins)) max_dev(rec + kRecTouched, kHistBins - from);
-  push_bins<T>(lh, from, ghist);
+  // the row's histogram, 16 bins to one: few device atomics per member, and a
+  // coarse threshold bucket that the tie list absorbs
+  push_coarse<T>(lh, ghist);
   group_sync(rec + kRecBarrier, static_cast<uint32_t>(G) * ++nbar, err);
-  read_bins<T>(ghist, sel.kk, sm.sel);
-  narrow(sel, sm.sel.res, s0);
+  {
+    const uint3 c = find_coarse(ghist, sel.kk);
+    const uint32_t res[3] = {c.x, c.y, c.z};
+    narrow(sel, res, s0 + (kHistBits - kCoarseBits));
+  }
 
   // ---- further rounds while the bucket exceeds the tie list
   int round = 1;
@@ -1148,8 +1191,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
       // the previous round's table is read by every member by now and is next
       // used two rounds on, after this member's next arrival
       const int prev = round - 1;
-      clear_bins<T>(ghist + (prev % 3) * kHistBins,
-                    prev == 0 ? kHistBins - ld_dev(rec + kRecTouched) : 0u);
+      clear_bins<T>(ghist + (prev % 3) * kHistBins, prev == 0 ? kCoarseBins : kHistBins);
     }
     read_bins<T>(buf, sel.kk, sm.sel);
     narrow(sel, sm.sel.res, s);
@@ -1308,16 +1350,14 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
                  [&](uint32_t slot, int32_t pos) { r.out[slot] = map_any(pos); });
 
   // ---- return the row's workspace to zero: the last round's table (round 0:
-  // only its touched range; earlier rounds were cleared on the way) and the record
-  const uint32_t touched = ld_dev(rec + kRecTouched);
+  // its coarse bins; earlier rounds were cleared on the way) and the record
   const int lastr = round - 1;
-  clear_bins<T>(ghist + (lastr % 3) * kHistBins, lastr == 0 ? kHistBins - touched : 0u);
+  clear_bins<T>(ghist + (lastr % 3) * kHistBins, lastr == 0 ? kCoarseBins : kHistBins);
   __syncthreads();  // every wave has read the record before it is reset
   if (tid == 0) {
     st_dev(rec + kRecBarrier, 0u);
     st_dev(rec + kRecDone, 0u);
     st_dev(reinterpret_cast<uint64_t*>(rec + kRecCursor), 0ull);
-    st_dev(rec + kRecTouched, 0u);
     st_dev(rec + kRecLb, 0u);
     st_dev(rec + kRecHi, 0u);
   }
@@ -1363,6 +1403,40 @@ __global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, i
 __global__ __launch_bounds__(256) void workspace_clear(uint32_t* ws, int64_t words) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < words; i += 256ll * gridDim.x) ws[i] = 0u;
 }
+
+// ---------------------------------------------------------------- measurement floors
+
+// The read alone: the grid, lane layout and loads of a selection launch.
+// Workgroup blockIdx.x takes chunk g of row b (G = 1: the whole row), forms
+// the keys and writes the chunk's largest key to sink[blockIdx.x]; nothing
+// else.
+template <int T, int VEC, int MODE, bool V4>
+__global__ __launch_bounds__(T) void floor_read_kernel(Params p, uint32_t* sink, int32_t G) {
+  using SpanT = Span<T, VEC, V4>;
+  __shared__ uint32_t red[T / 64];
+  const int b = static_cast<int>(blockIdx.x / static_cast<uint32_t>(G));
+  const int g = static_cast<int>(blockIdx.x % static_cast<uint32_t>(G));
+  const RowRef<MODE> r(p, b);
+  const int64_t chunk = ((static_cast<int64_t>(r.n) + G - 1) / G + 3) & ~static_cast<int64_t>(3);
+  const int32_t start = static_cast<int32_t>(min(static_cast<int64_t>(g) * chunk, static_cast<int64_t>(r.n)));
+  const int32_t end = (g == G - 1) ? r.n : static_cast<int32_t>(min(start + chunk, static_cast<int64_t>(r.n)));
+  const SpanT span{r.row, start, end};
+  uint32_t key[SpanT::PT];
+  uint32_t m = 0;
+  span.template for_each<false>(key, [&](uint32_t x, int32_t, int) { m = max(m, x); });
+  m = wave_reduce(m, OpMax());
+  if (__lane_id() == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < T / 64; ++w) m = max(m, red[w]);
+    sink[blockIdx.x] = m;
+  }
+}
+
+// The launch alone: a selection launch's grid and workgroup size, no work.
+template <int T>
+__global__ __launch_bounds__(T) void floor_launch_kernel() {}
 
 }  // namespace ets
 
@@ -1471,46 +1545,139 @@ void launch_group(const ets::Params& p, int32_t B, int32_t G, void* ws, hipStrea
                      0, stream, p, static_cast<uint32_t*>(ws), B, G);
 }
 
+// Launch shape of a selection call: workgroups per row (1 = one per row on
+// the row kernel), lanes per workgroup, float4 per lane per tile, and whether
+// a one-workgroup row is streamed tile by tile instead of held in registers.
+// A row on one workgroup gets the smallest resident tile that holds it, with
+// as few scores per lane as the lane count allows: the passes are latency
+// bound, and more waves with shorter slot loops hide more of it.
+struct Shape {
+  int32_t groups, threads, vec;
+  bool stream;
+};
+
+Shape launch_shape(int32_t B, int64_t max_len, int32_t cu_count) {
+  const int32_t G = split_plan(B, max_len, cu_count);
+  if (G == 0) {
+    if (max_len <= 2048) return {1, 512, 1, false};
+    if (max_len <= 4096) return {1, kRowThreads, 1, false};
+    if (max_len <= kRowTile / 4) return {1, kRowThreads, kRowVec / 4, false};
+    if (max_len <= kRowTile / 2) return {1, kRowThreads, kRowVec / 2, false};
+    return {1, kRowThreads, kRowVec, max_len > kRowTile};
+  }
+  const int64_t chunk = ((max_len + G - 1) / G + 3) / 4 * 4;
+  const int32_t vec = chunk <= kGroupThreads * 4 ? 1 : chunk <= kGroupThreads * 8 ? 2
+                    : chunk <= kGroupThreads * 16 ? 4 : 8;
+  return {G, kGroupThreads, vec, false};
+}
+
 template <int MODE, bool V4>
 ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, int32_t cu_count, void* ws,
                   hipStream_t stream) {
-  const int32_t G = split_plan(B, max_len, cu_count);
-  if (G == 0) {
-    // the smallest resident tile that holds the row, with as few scores per
-    // lane as the lane count allows: the passes are latency bound, and more
-    // waves with shorter slot loops hide more of it
-    if (max_len <= 2048) {
+  const Shape sh = launch_shape(B, max_len, cu_count);
+  if (sh.groups == 1) {
+    if (sh.threads == 512) {
       launch_rows<MODE, V4, 512, 1, false>(p, B, stream);
-    } else if (max_len <= 4096) {
-      launch_rows<MODE, V4, kRowThreads, 1, false>(p, B, stream);
-    } else if (max_len <= kRowTile / 4) {
-      launch_rows<MODE, V4, kRowThreads, kRowVec / 4, false>(p, B, stream);
-    } else if (max_len <= kRowTile / 2) {
-      launch_rows<MODE, V4, kRowThreads, kRowVec / 2, false>(p, B, stream);
-    } else if (max_len <= kRowTile) {
-      launch_rows<MODE, V4, kRowThreads, kRowVec, false>(p, B, stream);
-    } else {
+    } else if (sh.stream) {
       launch_rows<MODE, V4, kRowThreads, kRowVec, true>(p, B, stream);
+    } else if (sh.vec == 1) {
+      launch_rows<MODE, V4, kRowThreads, 1, false>(p, B, stream);
+    } else if (sh.vec == 2) {
+      launch_rows<MODE, V4, kRowThreads, 2, false>(p, B, stream);
+    } else if (sh.vec == 4) {
+      launch_rows<MODE, V4, kRowThreads, 4, false>(p, B, stream);
+    } else {
+      launch_rows<MODE, V4, kRowThreads, 8, false>(p, B, stream);
     }
     return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
   }
   // (workspace already validated by check_workspace)
-  const int64_t chunk = ((max_len + G - 1) / G + 3) / 4 * 4;
-  if (chunk <= kGroupThreads * 4) {
-    launch_group<MODE, V4, 1>(p, B, G, ws, stream);
-  } else if (chunk <= kGroupThreads * 8) {
-    launch_group<MODE, V4, 2>(p, B, G, ws, stream);
-  } else if (chunk <= kGroupThreads * 16) {
-    launch_group<MODE, V4, 4>(p, B, G, ws, stream);
+  if (sh.vec == 1) {
+    launch_group<MODE, V4, 1>(p, B, sh.groups, ws, stream);
+  } else if (sh.vec == 2) {
+    launch_group<MODE, V4, 2>(p, B, sh.groups, ws, stream);
+  } else if (sh.vec == 4) {
+    launch_group<MODE, V4, 4>(p, B, sh.groups, ws, stream);
   } else {
-    launch_group<MODE, V4, 8>(p, B, G, ws, stream);
+    launch_group<MODE, V4, 8>(p, B, sh.groups, ws, stream);
   }
   return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
+}
+
+template <int MODE, bool V4, int T, int VEC>
+void launch_floor_read(const ets::Params& p, uint32_t grid, uint32_t* sink, int32_t G, hipStream_t s) {
+  hipLaunchKernelGGL((ets::floor_read_kernel<T, VEC, MODE, V4>), dim3(grid), dim3(T), 0, s, p, sink, G);
+}
+
+template <int MODE, bool V4>
+void floor_read(const ets::Params& p, const Shape& sh, uint32_t grid, uint32_t* sink, hipStream_t s) {
+  if (sh.threads == 512) {
+    launch_floor_read<MODE, V4, 512, 1>(p, grid, sink, sh.groups, s);
+  } else if (sh.vec == 1) {
+    launch_floor_read<MODE, V4, 1024, 1>(p, grid, sink, sh.groups, s);
+  } else if (sh.vec == 2) {
+    launch_floor_read<MODE, V4, 1024, 2>(p, grid, sink, sh.groups, s);
+  } else if (sh.vec == 4) {
+    launch_floor_read<MODE, V4, 1024, 4>(p, grid, sink, sh.groups, s);
+  } else {
+    launch_floor_read<MODE, V4, 1024, 8>(p, grid, sink, sh.groups, s);
+  }
 }
 
 }  // namespace
 
 extern "C" {
+
+ets_status ets_floor_read(const float* scores, int64_t row_stride, int32_t B, int32_t L,
+                          const int32_t* lens, const int32_t* row_starts, int64_t max_len_hint,
+                          uint32_t* sink, int64_t sink_words, void* stream) {
+  const bool ragged = row_starts != nullptr;
+  if (B < 0 || (ragged ? (max_len_hint < 0 || !lens) : (L < 0 || row_stride < L)))
+    return ETS_ERR_INVALID_ARG;
+  if (B == 0) return ETS_OK;
+  if (!sink || !scores) return ETS_ERR_INVALID_ARG;
+  int dev;
+  DeviceInfo info;
+  if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
+  const int64_t max_len = ragged ? max_len_hint : L;
+  const Shape sh = launch_shape(B, max_len, info.cu_count);
+  const int64_t grid = static_cast<int64_t>(B) * sh.groups;
+  if (grid > INT32_MAX || sink_words < grid) return ETS_ERR_INVALID_ARG;
+  ets::Params p{};
+  p.scores = scores;
+  p.row_stride = row_stride;
+  p.lens = lens;
+  p.row_starts = row_starts;
+  p.L = L;
+  auto s = static_cast<hipStream_t>(stream);
+  const uint32_t g = static_cast<uint32_t>(grid);
+  if (ragged) {
+    floor_read<ets::kRagged, false>(p, sh, g, sink, s);
+  } else if (aligned16(scores) && row_stride % 4 == 0 && L % 4 == 0) {
+    floor_read<ets::kRaw, true>(p, sh, g, sink, s);
+  } else {
+    floor_read<ets::kRaw, false>(p, sh, g, sink, s);
+  }
+  return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
+}
+
+ets_status ets_floor_launch(int32_t B, int64_t max_row_len, void* stream) {
+  if (B < 0 || max_row_len < 0) return ETS_ERR_INVALID_ARG;
+  if (B == 0) return ETS_OK;
+  int dev;
+  DeviceInfo info;
+  if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
+  const Shape sh = launch_shape(B, max_row_len, info.cu_count);
+  const int64_t grid = static_cast<int64_t>(B) * sh.groups;
+  if (grid > INT32_MAX) return ETS_ERR_INVALID_ARG;
+  auto s = static_cast<hipStream_t>(stream);
+  if (sh.threads == 512) {
+    hipLaunchKernelGGL(ets::floor_launch_kernel<512>, dim3(static_cast<uint32_t>(grid)), dim3(512), 0, s);
+  } else {
+    hipLaunchKernelGGL(ets::floor_launch_kernel<1024>, dim3(static_cast<uint32_t>(grid)), dim3(1024), 0, s);
+  }
+  return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
+}
 
 const char* ets_status_string(ets_status status) {
   switch (status) {

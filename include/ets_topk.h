@@ -149,6 +149,30 @@ ets_status ets_workspace_init(void* workspace, size_t bytes, void* stream);
  */
 int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count);
 
+/*
+ * Measurement floors.  Neither selects anything: they give the cost of the
+ * parts of a selection call that no selection method avoids, so that a
+ * selection's time can be read against them.
+ *
+ * ets_floor_read: reads the same scores with the same grid, workgroup size,
+ * lane layout and loads as a selection call on (B, rows) would, forms the
+ * keys, and writes to sink[w] the largest key of the span that workgroup w
+ * read (chunk g of row b for w = b * G + g, G = max(1, ets_row_split(...))).
+ *   Dense rows (row_starts == NULL): scores, row_stride, B, L and lens
+ *   (nullable) as for ets_topk_raw; max_len_hint is ignored.
+ *   Ragged rows (row_starts != NULL): scores is the packed buffer, lens the
+ *   required lengths and max_len_hint as for ets_topk_ragged; row_stride and
+ *   L are ignored.
+ *   sink  uint32 [sink_words], sink_words >= B * G.
+ *
+ * ets_floor_launch: one launch of the grid and workgroup size a selection
+ * call on (B, max_row_len) uses, with empty workgroups.
+ */
+ets_status ets_floor_read(const float* scores, int64_t row_stride, int32_t B, int32_t L,
+                          const int32_t* lens, const int32_t* row_starts, int64_t max_len_hint,
+                          uint32_t* sink, int64_t sink_words, void* stream);
+ets_status ets_floor_launch(int32_t B, int64_t max_row_len, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* ets_status_string(ets_status status);
 

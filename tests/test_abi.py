@@ -77,6 +77,23 @@ def test_host_validation_rejects_before_device_work(lib):
     assert lib.ets_topk_raw(None, 0, 0, 0, None, 8, None, 8, None, 0, None) == 0
 
 
+def test_floor_validation(lib):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    # dense: negative batch or length, stride below L, missing sink or scores
+    assert lib.ets_floor_read(fake, 64, -1, 64, None, None, 0, fake, 64, None) == 1
+    assert lib.ets_floor_read(fake, 32, 1, 64, None, None, 0, fake, 64, None) == 1
+    assert lib.ets_floor_read(fake, 64, 1, 64, None, None, 0, None, 64, None) == 1
+    assert lib.ets_floor_read(None, 64, 1, 64, None, None, 0, fake, 64, None) == 1
+    # ragged: lengths required, hint >= 0
+    assert lib.ets_floor_read(fake, 0, 1, 0, None, fake, 10, fake, 64, None) == 1
+    assert lib.ets_floor_read(fake, 0, 1, 0, fake, fake, -1, fake, 64, None) == 1
+    # empty batches need no device
+    assert lib.ets_floor_read(None, 0, 0, 0, None, None, 0, None, 0, None) == 0
+    assert lib.ets_floor_launch(0, 100, None) == 0
+    assert lib.ets_floor_launch(-1, 100, None) == 1
+    assert lib.ets_floor_launch(1, -1, None) == 1
+
+
 def test_workspace_query_validation(lib):
     n = ctypes.c_size_t(123)
     assert lib.ets_workspace_size(4, 1000, 0, -1, ctypes.byref(n)) == 2
