@@ -839,7 +839,10 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // records and the tables to zero (tie lists may keep stale entries).
 
 constexpr int kTieCap = 4096;      // tie-list entries per row
-constexpr int kCoarseBits = 8;     // round 0 exchanges 2^kCoarseBits bins per row
+// Round 0 exchanges 2^kCoarseBits bins per row.  Measured on MI355X for rows
+// of 65536 to 262144 scores: 256 bins beat 64 (larger tie lists) and 1024
+// (more device atomics), and packed bins beat bins spread over more lines.
+constexpr int kCoarseBits = 8;
 constexpr int kCoarseBins = 1 << kCoarseBits;
 constexpr int kFinePerCoarse = kHistBins / kCoarseBins;
 constexpr int kGroupPtCap = 1024;  // chunk page-table entries staged in LDS
@@ -951,35 +954,52 @@ __device__ __forceinline__ void clear_bins(uint32_t* buf, uint32_t count) {
 // coarse table dst (device atomics; zero bins are skipped) and clears it.
 template <int T>
 __device__ __forceinline__ void push_coarse(uint32_t* lh, uint32_t* dst) {
-  static_assert(kHistBins / T == 4 && kFinePerCoarse == 16, "a quad of lanes holds one coarse bin");
+  constexpr int LPC = kFinePerCoarse / 4;  // lanes per coarse bin
+  static_assert(kHistBins / T == 4 && (LPC == 1 || LPC == 4 || LPC == 16), "lanes per coarse bin");
   uint4* q = reinterpret_cast<uint4*>(lh) + threadIdx.x;
   const uint4 c = *q;
   *q = make_uint4(0u, 0u, 0u, 0u);
   uint32_t v = (c.x + c.y) + (c.z + c.w);
-  v += dpp_perm<0xB1>(v);  // quad_perm [1,0,3,2]
-  v += dpp_perm<0x4E>(v);  // quad_perm [2,3,0,1]
-  if ((threadIdx.x & 3u) == 0 && v != 0) add_dev(dst + (threadIdx.x >> 2), v);
+  if constexpr (LPC >= 4) {
+    v += dpp_perm<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp_perm<0x4E>(v);  // quad_perm [2,3,0,1]
+  }
+  if constexpr (LPC >= 16) {
+    v += dpp_perm<0x141>(v);  // row_half_mirror
+    v += dpp_perm<0x140>(v);  // row_mirror
+  }
+  if ((threadIdx.x % LPC) == 0 && v != 0) add_dev(dst + threadIdx.x / LPC, v);
 }
 
 // Every wave reads the coarse table src and finds its threshold bin for kk:
 // (bin, entries above it, entries in it), the same in every lane.  No barrier.
 __device__ __forceinline__ uint3 find_coarse(const uint32_t* src, uint32_t kk) {
-  static_assert(kCoarseBins == 4 * 64, "a lane holds four coarse bins");
+  constexpr int C = kCoarseBins / 64;  // coarse bins per lane
+  static_assert(C * 64 == kCoarseBins && (C == 1 || C % 2 == 0), "coarse bins per lane");
   const uint32_t l = __lane_id();
-  const uint64_t a = ld_dev(reinterpret_cast<const uint64_t*>(src + 4 * l));
-  const uint64_t b = ld_dev(reinterpret_cast<const uint64_t*>(src + 4 * l + 2));
-  const uint32_t h[4] = {static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32),
-                         static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32)};
-  const uint32_t sum = (h[0] + h[1]) + (h[2] + h[3]);
+  uint32_t h[C];
+  if constexpr (C >= 2) {
+#pragma unroll
+    for (int i = 0; i < C; i += 2) {
+      const uint64_t a = ld_dev(reinterpret_cast<const uint64_t*>(src + C * l + i));
+      h[i] = static_cast<uint32_t>(a);
+      h[i + 1] = static_cast<uint32_t>(a >> 32);
+    }
+  } else {
+    h[0] = ld_dev(src + l);
+  }
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < C; ++i) sum += h[i];
   const uint32_t incl = wave_incl_scan(sum);
   uint32_t above = readlane(incl, 63) - incl;  // entries in higher lanes' bins
   uint32_t t = 0, ta = 0, th = 0;
   bool hit = false;
 #pragma unroll
-  for (int i = 3; i >= 0; --i) {
+  for (int i = C - 1; i >= 0; --i) {
     if (!hit && above < kk && kk <= above + h[i]) {
       hit = true;
-      t = 4 * l + i;
+      t = C * l + i;
       ta = above;
       th = h[i];
     }
@@ -1363,14 +1383,23 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   }
 }
 
-// One launch for the whole batch: B * G workgroups, G per row.
-template <int T, int VEC, int MODE, bool V4>
+// One launch for the whole batch: B * G workgroups, G per row.  TICKET:
+// workgroups take rows in the order they start (a device counter), so that
+// a group only waits for members that have started or start next and
+// progress needs room for one group.  Otherwise workgroup i is member i % G
+// of row i / G; the host chooses this only when the whole grid fits the
+// device at once (one workgroup per compute unit), where waiting members
+// can never keep the rest of the grid from starting.
+template <int T, int VEC, int MODE, bool V4, bool TICKET>
 __global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, int32_t B, int32_t G) {
   __shared__ GroupSmem sm;
   const GroupWs w(ws);
-  if (threadIdx.x == 0) sm.ticket = add_dev(w.hdr + kHdrTicket, 1u);
-  __syncthreads();
-  const uint32_t ticket = sm.ticket;
+  uint32_t ticket = blockIdx.x;
+  if constexpr (TICKET) {
+    if (threadIdx.x == 0) sm.ticket = add_dev(w.hdr + kHdrTicket, 1u);
+    __syncthreads();
+    ticket = sm.ticket;
+  }
   const int b = static_cast<int>(ticket / static_cast<uint32_t>(G));
   const int g = static_cast<int>(ticket % static_cast<uint32_t>(G));
   if (b < B) {  // always, unless the workspace was not zero
@@ -1391,11 +1420,13 @@ __global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, i
     }
   }
   // the last workgroup to finish re-arms the ticket counter for the next call
-  drain_vmem();
-  __syncthreads();
-  if (threadIdx.x == 0 && add_dev(w.hdr + kHdrFinished, 1u) == gridDim.x - 1) {
-    st_dev(w.hdr + kHdrTicket, 0u);
-    st_dev(w.hdr + kHdrFinished, 0u);
+  if constexpr (TICKET) {
+    drain_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0 && add_dev(w.hdr + kHdrFinished, 1u) == gridDim.x - 1) {
+      st_dev(w.hdr + kHdrTicket, 0u);
+      st_dev(w.hdr + kHdrFinished, 0u);
+    }
   }
 }
 
@@ -1539,10 +1570,16 @@ void launch_rows(const ets::Params& p, int32_t B, hipStream_t stream) {
 }
 
 template <int MODE, bool V4, int VEC>
-void launch_group(const ets::Params& p, int32_t B, int32_t G, void* ws, hipStream_t stream) {
-  hipLaunchKernelGGL((ets::group_topk_kernel<kGroupThreads, VEC, MODE, V4>),
-                     dim3(static_cast<uint32_t>(B) * static_cast<uint32_t>(G)), dim3(kGroupThreads),
-                     0, stream, p, static_cast<uint32_t*>(ws), B, G);
+void launch_group(const ets::Params& p, int32_t B, int32_t G, int32_t cu_count, void* ws,
+                  hipStream_t stream) {
+  const uint32_t grid = static_cast<uint32_t>(B) * static_cast<uint32_t>(G);
+  if (grid <= static_cast<uint32_t>(cu_count)) {
+    hipLaunchKernelGGL((ets::group_topk_kernel<kGroupThreads, VEC, MODE, V4, false>), dim3(grid),
+                       dim3(kGroupThreads), 0, stream, p, static_cast<uint32_t*>(ws), B, G);
+  } else {
+    hipLaunchKernelGGL((ets::group_topk_kernel<kGroupThreads, VEC, MODE, V4, true>), dim3(grid),
+                       dim3(kGroupThreads), 0, stream, p, static_cast<uint32_t*>(ws), B, G);
+  }
 }
 
 // Launch shape of a selection call: workgroups per row (1 = one per row on
@@ -1593,13 +1630,13 @@ ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, int32_t cu_c
   }
   // (workspace already validated by check_workspace)
   if (sh.vec == 1) {
-    launch_group<MODE, V4, 1>(p, B, sh.groups, ws, stream);
+    launch_group<MODE, V4, 1>(p, B, sh.groups, cu_count, ws, stream);
   } else if (sh.vec == 2) {
-    launch_group<MODE, V4, 2>(p, B, sh.groups, ws, stream);
+    launch_group<MODE, V4, 2>(p, B, sh.groups, cu_count, ws, stream);
   } else if (sh.vec == 4) {
-    launch_group<MODE, V4, 4>(p, B, sh.groups, ws, stream);
+    launch_group<MODE, V4, 4>(p, B, sh.groups, cu_count, ws, stream);
   } else {
-    launch_group<MODE, V4, 8>(p, B, sh.groups, ws, stream);
+    launch_group<MODE, V4, 8>(p, B, sh.groups, cu_count, ws, stream);
   }
   return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
 }
