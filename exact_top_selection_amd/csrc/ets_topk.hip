@@ -1269,10 +1269,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     sm.base[1] = static_cast<uint32_t>(old);
     sm.wcount = ow + nw;
   }
-  __syncthreads();
-  const uint32_t wbase = sm.base[0];
-  const uint32_t wtot = sm.wcount;
-  ob += sm.base[1];
+  // the winners' chunk-local slots need no cursor: placed while it returns
   if constexpr (RES) {
     while (wmask != 0) {
       const int j = PT - __ffs(static_cast<int>(wmask));
@@ -1280,6 +1277,19 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
       if (ow < static_cast<uint32_t>(ETS_MAX_K)) sm.u.pos[ow] = span.start + tile_pos<T, V4>(j);
       ++ow;
     }
+  } else {
+    for_each([&](uint32_t x, int32_t pos, int) {
+      if (sel_winner(sel, nm1, cend, x, pos)) {
+        if (ow < static_cast<uint32_t>(ETS_MAX_K)) sm.u.pos[ow] = pos;
+        ++ow;
+      }
+    });
+  }
+  __syncthreads();
+  const uint32_t wbase = sm.base[0];
+  const uint32_t wtot = sm.wcount;
+  ob += sm.base[1];
+  if constexpr (RES) {
     while (cmask != 0) {
       const int j = PT - __ffs(static_cast<int>(cmask));
       cmask &= cmask - 1u;
@@ -1290,10 +1300,6 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     }
   } else {
     for_each([&](uint32_t x, int32_t pos, int) {
-      if (sel_winner(sel, nm1, cend, x, pos)) {
-        if (ow < static_cast<uint32_t>(ETS_MAX_K)) sm.u.pos[ow] = pos;
-        ++ow;
-      }
       if (sel_bucket(sel, nm1, cend, x, pos)) {
         if (ob < static_cast<uint32_t>(kTieCap))
           st_dev(gties + ob, (static_cast<uint64_t>(x) << 32) | static_cast<uint32_t>(pos));
@@ -1301,7 +1307,6 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
       }
     });
   }
-  __syncthreads();
   // winners through the output map, contiguous stores
   auto map_any = [&](int32_t pos) {
     return out_value<MODE>(p, false, nullptr, r.pt_row, r.row_start, pos);
