@@ -114,6 +114,10 @@ __device__ __forceinline__ uint32_t shift_in_le(uint32_t mask, uint32_t a, uint3
   asm("v_cmp_le_u32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc" : "+v"(mask) : "v"(a), "v"(b) : "vcc");
   return mask;
 }
+__device__ __forceinline__ uint32_t shift_in_eq(uint32_t mask, uint32_t a, uint32_t b) {
+  asm("v_cmp_eq_u32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc" : "+v"(mask) : "v"(a), "v"(b) : "vcc");
+  return mask;
+}
 
 struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
 struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
@@ -140,16 +144,44 @@ __device__ __forceinline__ uint32_t sum_other_waves(const uint32_t* wsum) {
   return wave_reduce(take ? v : 0u, OpAdd());
 }
 
-// Adds one to hist[bin] for every lane with `pred` (call in uniform control
-// flow).  Lanes that share lane 0's bin are merged into one LDS atomic issued
-// by lane 0, which removes the serialisation when most of a wave lands in one
-// bin (concentrated scores); the other lanes add individually.
-__device__ __forceinline__ void hist_add_peel(uint32_t* hist, bool pred, uint32_t bin) {
-  const uint32_t lead = readfirstlane(bin);
-  const bool same = pred && bin == lead;
-  const uint64_t m = __ballot(same);
-  if (__lane_id() == 0 && m != 0) atomicAdd(&hist[lead], static_cast<uint32_t>(__popcll(m)));
-  if (pred && !same) atomicAdd(&hist[bin], 1u);
+// One histogram pass over the keys of for_each into hist (bins of d =
+// x - lo, d <= span, shifted by s; out-of-range keys go to the lane's dummy
+// bin) for a wave whose lanes pile into one `hot` bin: each lane counts its
+// hot keys in a register and sends them to its dummy bin instead, and the
+// wave adds the hot count once, so that the pile causes no serialised LDS
+// atomics (and no per-key scalar work).  Call in uniform control flow.
+template <class ForEach>
+__device__ __forceinline__ void hist_pass_hot(ForEach&& for_each, uint32_t* hist, uint32_t lo,
+                                              uint32_t span, int s, uint32_t hot) {
+  const uint32_t dummy = kHistBins + __lane_id();
+  uint32_t cnt = 0;
+  for_each([&](uint32_t x, int32_t, int) {
+    const uint32_t d = x - lo;
+    const uint32_t b = d <= span ? d >> s : dummy;
+    const bool h = b == hot;
+    cnt += h ? 1u : 0u;
+    atomicAdd(&hist[h ? dummy : b], 1u);
+  });
+  cnt = wave_reduce(cnt, OpAdd());
+  if (__lane_id() == 0 && cnt != 0) atomicAdd(&hist[hot], cnt);
+}
+
+// The wave's hot bin for a round: of the bins of lanes 0, 16, 32 and 48 (one
+// probe slot each), the one most lanes share, with that lane count.  One
+// probe lane holding an outlier no longer hides a bin that the rest of the
+// wave piles into.
+__device__ __forceinline__ uint2 wave_hot_bin(bool pred, uint32_t bin) {
+  uint32_t best = 0, count = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t cand = readlane(bin, 16 * c);
+    const uint32_t n = static_cast<uint32_t>(__popcll(__ballot(pred && bin == cand)));
+    if (n > count) {
+      count = n;
+      best = cand;
+    }
+  }
+  return make_uint2(best, count);
 }
 
 // Finds the histogram bin t with above(t) < kk <= above(t) + hist[t], where
@@ -364,12 +396,15 @@ __device__ __forceinline__ void hist_clear(uint32_t* hist) {
 // lowest positions win.  Padding slots have pos >= n: their d wraps far
 // above any range.  Round r counts into hist[r & 1] and clears the other
 // buffer.  Precondition: hist[round & 1] is zero and a barrier has passed.
-// Each wave probes (with probe_key) whether its lanes pile into one bin and
-// only then merges its LDS atomics.  Precondition: no key that for_each
-// visits lies above in.hi.  Returns the refined state.
+// Each wave probes (with probe_key) whether its lanes pile into one hot bin
+// and only then merges the atomics into it.  Without tie_rounds, a key left
+// with too many ties is returned as is (tie = 1, bucket = its count) for the
+// caller to resolve by position.  Precondition: no key that for_each visits
+// lies above in.hi.  Returns the refined state.
 template <int T, class ForEach>
 __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel in, uint32_t nm1,
-                                      uint32_t n_pad, uint32_t probe_key, int& round) {
+                                      uint32_t n_pad, uint32_t probe_key, int& round,
+                                      bool tie_rounds = true) {
   uint32_t lo = in.lo, hi = in.hi, kk = in.kk, bucket = in.bucket;
   uint32_t tie = 0, dlo = 0, dhi = nm1;
   const int first_round = round;
@@ -379,18 +414,10 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
     const uint32_t rlo = lo, span = hi - lo;
     const int bl = span ? 32 - __clz(static_cast<int>(span)) : 0;
     const int s = bl > kHistBits ? bl - kHistBits : 0;
-    bool peel;
-    {
-      const uint32_t d = probe_key - rlo;
-      const uint32_t bin = d >> s;
-      const uint32_t lead = readfirstlane(bin);
-      peel = __popcll(__ballot(d <= span && bin == lead)) > kPeelShare;
-    }
-    if (peel) {
-      for_each([&](uint32_t x, int32_t, int) {
-        const uint32_t d = x - rlo;
-        hist_add_peel(hist, d <= span, d >> s);
-      });
+    const uint32_t pd = probe_key - rlo;
+    const uint2 hot = wave_hot_bin(pd <= span, pd >> s);
+    if (hot.y > kPeelShare) {
+      hist_pass_hot(for_each, hist, rlo, span, s, hot.x);
     } else if (round == first_round && rlo != 0 && ((0u - rlo) >> s) >= kHistBins + 64) {
       // First round: nothing lies above hi, and a key under lo wraps to a
       // difference whose bin lies past every lane's dummy, so a min picks the
@@ -418,7 +445,7 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
   if (bucket > static_cast<uint32_t>(kSmallCap)) {
     tie = 1;
     const uint32_t tkey = lo;
-    while (bucket > static_cast<uint32_t>(kSmallCap) && round < kMaxRounds) {
+    while (tie_rounds && bucket > static_cast<uint32_t>(kSmallCap) && round < kMaxRounds) {
       uint32_t* hist = sm.hist[round & 1];
       hist_clear<T>(sm.hist[(round + 1) & 1]);
       const uint32_t rdlo = dlo, span = dhi - dlo;
@@ -676,12 +703,18 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
   // ---- radix refinement until the bucket is small
   const uint32_t nm1 = static_cast<uint32_t>(n - 1);
   int round = 0;
-  const Sel sel = refine<T>(for_each, sm.sel, sel0, nm1, span.pad_slots(), key[0], round);
+  // a resident row in float4 layout resolves a key with too many ties by the
+  // positions' prefix counts instead of radix rounds on positions
+  constexpr bool kPrefixTies = V4 && !STREAM;
+  const Sel sel = refine<T>(for_each, sm.sel, sel0, nm1, span.pad_slots(), key[0], round,
+                            !kPrefixTies);
+  const bool prefix_ties = kPrefixTies && sel.tie && sel.bucket > static_cast<uint32_t>(kSmallCap);
 
   // ---- scatter: append the bucket to LDS, count the winners, place them by
   // one block scan (whose barrier also publishes the bucket) into the
   // position list.
-  const uint32_t first = static_cast<uint32_t>(k) - sel.kk;  // number of winners
+  // number of winners placed by the scatter (the rest come from the bucket)
+  const uint32_t first = prefix_ties ? static_cast<uint32_t>(k) : static_cast<uint32_t>(k) - sel.kk;
   // the page-table source is chosen once per row, so that each emitting loop
   // reads only LDS (or only global memory) and never waits on its stores
   auto emitter = [&](auto lds) {
@@ -704,7 +737,61 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
     // bit PT-1-j of wmask / cmask: slot j is a winner / in the bucket
     static_assert(PT <= 32, "slot masks are 32 bits");
     uint32_t wmask = 0, cmask = 0;
-    if (!sel.tie) {
+    if (prefix_ties) {
+      // One key T with more than kSmallCap copies: its sel.kk copies at the
+      // lowest positions win.  Positions grow with (group v of four slots,
+      // lane, slot c in the group).  Block totals per group name the group
+      // v* that holds the kk-th copy; one block scan of that group's counts
+      // over the lanes then tells each lane how many of its copies there
+      // win.  Copies in lower groups all win.  Padding lies past every
+      // position, hence after every copy.
+      static_assert(PT == 4 * VEC && W <= 16, "float4 groups, at most 16 waves");
+      constexpr int NW = (VEC + 1) / 2;
+      const uint32_t tkey = sel.hi;
+      uint32_t emask = 0;
+      for_each([&](uint32_t x, int32_t, int) {
+        wmask = shift_in_lt(wmask, tkey, x);
+        emask = shift_in_eq(emask, x, tkey);
+      });
+      // group v's slot c sits at bit 3 - c of its nibble
+      auto nib = [&](int v) { return (emask >> (PT - 4 - 4 * v)) & 0xFu; };
+      if (tid < NW) sm.red[tid] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const uint32_t c0 = static_cast<uint32_t>(__popc(nib(2 * i)));
+        const uint32_t c1 = 2 * i + 1 < VEC ? static_cast<uint32_t>(__popc(nib(2 * i + 1))) : 0u;
+        // two 16-bit fields: a block holds at most 4 * T <= 4096 copies per group
+        const uint32_t ws = wave_reduce(c0 | (c1 << 16), OpAdd());
+        if (__lane_id() == 0 && ws != 0) atomicAdd(&sm.red[i], ws);
+      }
+      __syncthreads();
+      uint32_t need = sel.kk, vstar = 0;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const uint32_t tot = (sm.red[v / 2] >> (16 * (v & 1))) & 0xFFFFu;
+        if (vstar == static_cast<uint32_t>(v) && need > tot) {
+          need -= tot;
+          ++vstar;
+        }
+      }
+      // vstar < VEC: the bucket holds kk or more copies
+      const uint32_t shift = PT - 4 - 4 * vstar;
+      const uint32_t e = (emask >> shift) & 0xFu;
+      const uint32_t cnt = static_cast<uint32_t>(__popc(e));
+      const uint32_t incl = wave_incl_scan(cnt);
+      if (__lane_id() == 63) sm.sel.wsum[wid] = incl;
+      __syncthreads();
+      const uint32_t ex = incl - cnt + sum_other_waves<W, true>(sm.sel.wsum);
+      const uint32_t r = need > ex ? min(need - ex, cnt) : 0u;  // this lane's winning copies in v*
+      uint32_t top = e;  // its r highest set bits: drop the lowest cnt - r
+#pragma unroll
+      for (int q = 1; q <= 4; ++q)
+        if (cnt - r >= static_cast<uint32_t>(q)) top &= top - 1u;
+      const uint32_t lower = vstar == 0 ? 0u : ~0u << (PT - 4 * vstar);  // groups below v*
+      wmask |= (emask & lower) | (top << shift);
+      __syncthreads();  // sm.red and wsum are free again
+    } else if (!sel.tie) {
       const uint32_t khi = sel.hi, klo = sel.lo, kspan = sel.hi - sel.lo;
       if (klo != 0) {
         for_each([&](uint32_t x, int32_t, int) {
@@ -1138,14 +1225,10 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     s0 = digit_shift(span_k);
     const int s = s0;
     const uint32_t pd = (RES ? key[0] : 0u) - lo;
-    const uint32_t pbin = pd >> s;
-    const bool peel = __popcll(__ballot(pd <= span_k && pbin == readfirstlane(pbin))) > kPeelShare;
+    const uint2 hot = wave_hot_bin(pd <= span_k, pd >> s);
     const uint32_t dummy = kHistBins + __lane_id();
-    if (peel) {
-      for_each([&](uint32_t x, int32_t, int) {
-        const uint32_t d = x - lo;
-        hist_add_peel(lh, d <= span_k, d >> s);
-      });
+    if (hot.y > kPeelShare) {
+      hist_pass_hot(for_each, lh, lo, span_k, s, hot.x);
     } else if (lo != 0 && ((0u - lo) >> s) >= kHistBins + 64) {
       // nothing lies above hi, and a key under lo wraps past every dummy
       for_each([&](uint32_t x, int32_t, int) { atomicAdd(&lh[min((x - lo) >> s, dummy)], 1u); });
@@ -1179,13 +1262,9 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
       const uint32_t lo = sel.lo, span_k = sel.hi - sel.lo;
       s = digit_shift(span_k);
       const uint32_t pd = (RES ? key[0] : 0u) - lo;
-      const uint32_t pbin = pd >> s;
-      const bool peel = __popcll(__ballot(pd <= span_k && pbin == readfirstlane(pbin))) > kPeelShare;
-      if (peel) {
-        for_each([&](uint32_t x, int32_t, int) {
-          const uint32_t d = x - lo;
-          hist_add_peel(lh, d <= span_k, d >> s);
-        });
+      const uint2 hot = wave_hot_bin(pd <= span_k, pd >> s);
+      if (hot.y > kPeelShare) {
+        hist_pass_hot(for_each, lh, lo, span_k, s, hot.x);
       } else {
         const uint32_t dummy = kHistBins + __lane_id();
         for_each([&](uint32_t x, int32_t, int) {
@@ -1201,7 +1280,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
       const int32_t end = span.end;
       for_each([&](uint32_t x, int32_t pos, int) {
         const uint32_t d = nm1 - static_cast<uint32_t>(pos) - dlo;
-        hist_add_peel(lh, x == tkey && pos < end && d <= span_d, d >> s);
+        if (x == tkey && pos < end && d <= span_d) atomicAdd(&lh[d >> s], 1u);
       });
     }
     __syncthreads();

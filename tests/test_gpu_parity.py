@@ -129,6 +129,22 @@ def test_heavy_ties(pool):
         assert_parity(w, run_gpu(w), run_oracle(w))
 
 
+def test_ties_at_the_lowest_key():
+    """Ties on key 0 (bit pattern 0xFFFFFFFF), the key the padding slots also
+    hold: rows whose length is not a multiple of 4 must still take the
+    lowest real positions."""
+    rng = np.random.default_rng(8)
+    L = 32768
+    bits = np.full((4, L), 0xFFFFFFFF, dtype=np.uint32)
+    bits[1, rng.integers(0, L, size=700)] = np.float32(2.0).view(np.uint32)
+    bits[2, ::3] = np.float32(-1.0).view(np.uint32)
+    x = bits.view(np.float32)
+    lens = np.array([32767, 30001, 4097, 2050], dtype=np.int32)
+    for k in (1, 1024, 2048):
+        w = _dense("key0-ties", "raw", x, k, lens)
+        assert_parity(w, run_gpu(w), run_oracle(w))
+
+
 def test_concentrated_rows_small_batch():
     rng = np.random.Generator(np.random.PCG64(9))
     x = np.stack([workloads.concentrated_row(rng, 32768) for _ in range(6)])
