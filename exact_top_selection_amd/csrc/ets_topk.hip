@@ -315,16 +315,15 @@ struct Span {
       for (int v = 0; v < VEC; ++v) {
         const int32_t g0 = base + 4 * v * T;  // first position of the group
         const int32_t q = g0 + 4 * tid;
+        if (g0 + 4 * T <= end) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uint32_t& x = key[4 * v + c];
-          if (g0 + 4 * T <= end) {
-            x = order_key(x);
-          } else if (g0 >= end) {
-            x = 0u;
-          } else {
-            x = q + c < end ? order_key(x) : 0u;
-          }
+          for (int c = 0; c < 4; ++c) key[4 * v + c] = order_key(key[4 * v + c]);
+        } else if (g0 >= end) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) key[4 * v + c] = 0u;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) key[4 * v + c] = q + c < end ? order_key(key[4 * v + c]) : 0u;
         }
       }
     } else {
