@@ -45,6 +45,15 @@ constexpr uint32_t kPeelShare = 16;  // lanes of a wave in one bin that switch t
 // Radix rounds needed at most: 12 + 12 + 8 key bits, then 12 + 12 + 7 position
 // bits; loops stop there even on inconsistent counts, so every kernel ends.
 constexpr int kMaxRounds = 8;
+#ifndef ETS_EARLY_FILL
+#define ETS_EARLY_FILL 2
+#endif
+// a resident row of at least kEarlyMinFill quarters of its tile takes the
+// bounds of its first round from the waves whose loads arrive first, unless
+// the range they leave puts up to 2^(s + log2 n - 23) > 2^(kEarlyMaxSpread -
+// 23) of its n scores into one octave's bin of 2^s keys
+constexpr int kEarlyMinFill = ETS_EARLY_FILL;
+constexpr int kEarlyMaxSpread = 32;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -294,39 +303,16 @@ struct Span {
   // wholly inside, straddle or lie past the end are told apart per group, the
   // same for all lanes.
   __device__ __forceinline__ void load(Keys& key, int32_t base) const {
-    const int32_t tid = static_cast<int32_t>(threadIdx.x);
     if (base >= end) {
 #pragma unroll
       for (int j = 0; j < PT; ++j) key[j] = 0u;
       return;
     }
     if constexpr (V4) {
-      const int32_t qlast = (end - 1) & ~3;
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const int32_t q = min(base + 4 * (v * T + tid), qlast);
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + q));
-        key[4 * v + 0] = w.x;
-        key[4 * v + 1] = w.y;
-        key[4 * v + 2] = w.z;
-        key[4 * v + 3] = w.w;
-      }
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const int32_t g0 = base + 4 * v * T;  // first position of the group
-        const int32_t q = g0 + 4 * tid;
-        if (g0 + 4 * T <= end) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) key[4 * v + c] = order_key(key[4 * v + c]);
-        } else if (g0 >= end) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) key[4 * v + c] = 0u;
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) key[4 * v + c] = q + c < end ? order_key(key[4 * v + c]) : 0u;
-        }
-      }
+      issue(key, base);
+      form(key, base);
     } else {
+      const int32_t tid = static_cast<int32_t>(threadIdx.x);
 #pragma unroll
       for (int j = 0; j < PT; ++j) {
         const int32_t q = min(base + j * T + tid, end - 1);
@@ -341,6 +327,44 @@ struct Span {
           key[j] = 0u;
         } else {
           key[j] = g0 + tid < end ? order_key(key[j]) : 0u;
+        }
+      }
+    }
+  }
+  // V4, base < end: the loads of load(), bit patterns into key; form() then
+  // waits for them and turns them into keys.  Between the two a wave may do
+  // other work (a barrier included) while its loads are in flight.
+  __device__ __forceinline__ void issue(Keys& key, int32_t base) const {
+    static_assert(V4, "float4 layout");
+    const int32_t tid = static_cast<int32_t>(threadIdx.x);
+    const int32_t qlast = (end - 1) & ~3;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const int32_t q = min(base + 4 * (v * T + tid), qlast);
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + q));
+      key[4 * v + 0] = w.x;
+      key[4 * v + 1] = w.y;
+      key[4 * v + 2] = w.z;
+      key[4 * v + 3] = w.w;
+    }
+  }
+  __device__ __forceinline__ void form(Keys& key, int32_t base) const {
+    static_assert(V4, "float4 layout");
+    const int32_t tid = static_cast<int32_t>(threadIdx.x);
+    {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const int32_t g0 = base + 4 * v * T;  // first position of the group
+        const int32_t q = g0 + 4 * tid;
+        if (g0 + 4 * T <= end) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) key[4 * v + c] = order_key(key[4 * v + c]);
+        } else if (g0 >= end) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) key[4 * v + c] = 0u;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) key[4 * v + c] = q + c < end ? order_key(key[4 * v + c]) : 0u;
         }
       }
     }
@@ -398,12 +422,13 @@ __device__ __forceinline__ void hist_clear(uint32_t* hist) {
 // Each wave probes (with probe_key) whether its lanes pile into one hot bin
 // and only then merges the atomics into it.  Without tie_rounds, a key left
 // with too many ties is returned as is (tie = 1, bucket = its count) for the
-// caller to resolve by position.  Precondition: no key that for_each visits
-// lies above in.hi.  Returns the refined state.
+// caller to resolve by position.  above_free: no key that for_each visits
+// lies above in.hi (otherwise keys above the range go to the dummy bins by a
+// range test in every round).  Returns the refined state.
 template <int T, class ForEach>
 __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel in, uint32_t nm1,
                                       uint32_t n_pad, uint32_t probe_key, int& round,
-                                      bool tie_rounds = true) {
+                                      bool tie_rounds = true, bool above_free = true) {
   uint32_t lo = in.lo, hi = in.hi, kk = in.kk, bucket = in.bucket;
   uint32_t tie = 0, dlo = 0, dhi = nm1;
   const int first_round = round;
@@ -417,7 +442,7 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
     const uint2 hot = wave_hot_bin(pd <= span, pd >> s);
     if (hot.y > kPeelShare) {
       hist_pass_hot(for_each, hist, rlo, span, s, hot.x);
-    } else if (round == first_round && rlo != 0 && ((0u - rlo) >> s) >= kHistBins + 64) {
+    } else if (above_free && round == first_round && rlo != 0 && ((0u - rlo) >> s) >= kHistBins + 64) {
       // First round: nothing lies above hi, and a key under lo wraps to a
       // difference whose bin lies past every lane's dummy, so a min picks the
       // dummy without a range test (in-range bins are the same as below).
@@ -590,6 +615,154 @@ __device__ __forceinline__ void emit_whole_row(const Params& p, const RowRef<MOD
 
 // ---------------------------------------------------------------- single-workgroup row kernel
 
+// First round of a resident float4 row (T = 1024) whose loads were issued
+// and formed into keys only by the first WB = W / 2 waves.  Bounds from
+// those waves' keys: their largest (hi), and a lower bound (lo) of the row's
+// k-th largest from the jth-largest keys of their lanes (jth = ceil(k /
+// lanes), at most 4), as in the whole-row bounds; 0 if too few lanes hold
+// jth scores.  Keys of the other waves may lie above hi, so the 12-bit
+// histogram of [lo, hi] keeps its last bin for every key from
+// lo + (kHistBins - 1) << s up.  The other waves form their keys in this
+// pass.  Returns the state after the round (a bucket of the last bin
+// reaches up to the largest key); hist[0] has been used, hist[1] is zero.
+template <int T, int VEC, class SpanT>
+__device__ __forceinline__ Sel early_round(const SpanT& span, uint32_t (&key)[4 * VEC], SelSmem& sm,
+                                           uint32_t* red, int32_t k, int32_t n) {
+  constexpr int PT = 4 * VEC;
+  constexpr int W = T / 64;
+  constexpr int WB = W / 2;
+  constexpr int LB = 64 * WB;  // lanes of the bounding waves
+  const int tid = threadIdx.x;
+  const int wid = tid >> 6;
+  const int32_t jth = (k + LB - 1) / LB;  // 1 .. 4 for k <= ETS_MAX_K
+  static_assert(ETS_MAX_K <= 4 * LB, "at most the 4th-largest key of a lane");
+  uint32_t m1 = 0, mj = 0;
+  if (wid < WB) {
+    if (jth <= 2) {
+      uint32_t m2 = 0;
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        m2 = max(m2, min(m1, key[j]));
+        m1 = max(m1, key[j]);
+      }
+      mj = jth == 1 ? m1 : m2;
+    } else {
+      uint32_t m2 = 0, m3 = 0, m4 = 0;
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const uint32_t x = key[j];
+        m4 = max(m4, min(m3, x));
+        m3 = max(m3, min(m2, x));
+        m2 = max(m2, min(m1, x));
+        m1 = max(m1, x);
+      }
+      mj = jth == 3 ? m3 : m4;
+    }
+    // lanes whose first jth slots (positions 4t .. 4t + jth - 1) hold scores
+    const bool full = 4 * tid + jth - 1 < n;
+    const uint32_t wmax = wave_reduce(m1, OpMax());
+    const uint32_t wlb = wave_reduce(full ? mj : 0xFFFFFFFFu, OpMin());
+    if (__lane_id() == 0) {
+      red[wid] = wmax;
+      red[16 + wid] = wlb;
+    }
+  }
+  hist_clear<T>(sm.hist[1]);
+  __syncthreads();
+  uint32_t hi = 0, lb = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < WB; ++w) {
+    hi = max(hi, red[w]);
+    lb = min(lb, red[16 + w]);
+  }
+  const int32_t nfull = min(LB, max(0, (n - jth) / 4 + 1));
+  uint32_t lo = nfull * jth >= k ? lb : 0u;
+  auto shift_of = [](uint32_t span) {
+    int sh = span ? 32 - __clz(static_cast<int>(span)) : 0;
+    sh = sh > kHistBits ? sh - kHistBits : 0;
+    if ((span >> sh) >= static_cast<uint32_t>(kHistBins - 1)) ++sh;  // [lo, hi] in bins below the last
+    return sh;
+  };
+  int s = shift_of(hi - lo);
+  bool formed = wid < WB;
+  if (s + (31 - __clz(n)) > kEarlyMaxSpread) {
+    // Too wide a range for the row (bins of 2^s keys, 2^(23 - s) to an
+    // octave of floats: with n >= 2^(kEarlyMaxSpread - s) scores a bin near
+    // the threshold may outgrow the bucket that is ranked directly; the
+    // range then reaches down many octaves, across zero say): take the
+    // whole-row bounds as well, the minimum over all lanes of their j2-th largest key, j2 =
+    // ceil(k / T) <= 2 (every lane holds two: n >= 4 T), and the largest key.
+    if (!formed) span.form(key, 0);
+    formed = true;
+    uint32_t a = 0, b2 = 0;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      b2 = max(b2, min(a, key[j]));
+      a = max(a, key[j]);
+    }
+    static_assert(ETS_MAX_K <= 2 * T, "two keys per lane bound the k-th largest");
+    const uint32_t wmax = wave_reduce(a, OpMax());
+    const uint32_t wmin = wave_reduce(k <= T ? a : b2, OpMin());
+    if (__lane_id() == 0) {
+      red[32 + wid] = wmax;
+      red[48 + wid] = wmin;
+    }
+    __syncthreads();
+    uint32_t lo2 = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      hi = max(hi, red[32 + w]);
+      lo2 = min(lo2, red[48 + w]);
+    }
+    lo = max(lo, lo2);
+    s = shift_of(hi - lo);
+  }
+  const uint64_t top = static_cast<uint64_t>(lo) + (static_cast<uint64_t>(kHistBins - 1) << s);
+  const uint32_t clampv = top > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(top);
+  // keys under lo wrap past every lane's dummy bin, or are tested
+  const bool wrap = lo != 0 && ((0u - lo) >> s) >= static_cast<uint32_t>(kHistBins + 64);
+  const uint32_t dummy = kHistBins + __lane_id();
+
+  if (!formed) span.form(key, 0);
+  uint32_t* hist = sm.hist[0];
+  auto bin = [&](uint32_t x) {
+    const uint32_t b = (min(x, clampv) - lo) >> s;
+    return wrap ? min(b, dummy) : (x >= lo ? b : dummy);
+  };
+  const uint32_t pb = bin(key[0]);
+  const uint2 hot = wave_hot_bin(pb < static_cast<uint32_t>(kHistBins), pb);
+  if (hot.y > kPeelShare) {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const uint32_t b = bin(key[j]);
+      const bool h = b == hot.x;
+      cnt += h ? 1u : 0u;
+      atomicAdd(&hist[h ? dummy : b], 1u);
+    }
+    cnt = wave_reduce(cnt, OpAdd());
+    if (__lane_id() == 0 && cnt != 0) atomicAdd(&hist[hot.x], cnt);
+  } else if (wrap) {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) atomicAdd(&hist[min((min(key[j], clampv) - lo) >> s, dummy)], 1u);
+  } else {
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const uint32_t x = key[j];
+      atomicAdd(&hist[x >= lo ? (min(x, clampv) - lo) >> s : dummy], 1u);
+    }
+  }
+  __syncthreads();
+  find_threshold_bin<T>(hist, static_cast<uint32_t>(k), lo == 0 ? span.pad_slots() : 0u, sm.wsum, sm.res);
+  Sel out{};
+  out.kk = static_cast<uint32_t>(k) - sm.res[1];
+  out.bucket = sm.res[2];
+  out.lo = lo + (sm.res[0] << s);
+  out.hi = sm.res[0] == static_cast<uint32_t>(kHistBins - 1) ? 0xFFFFFFFFu : out.lo + ((1u << s) - 1u);
+  out.dhi = static_cast<uint32_t>(n - 1);
+  return out;
+}
+
 struct alignas(16) RowSmem {
   SelSmem sel;
   int32_t pt[kPtCap];     // staged page-table row (paged map)
@@ -629,7 +802,24 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
 
   const SpanT span{r.row, 0, n};
   uint32_t key[PT];
-  if constexpr (!STREAM) span.load(key, 0);
+  // A resident float4 row takes the bounds of its first round from the
+  // first WB waves, whose loads the compute unit serves first, and the
+  // other waves form their keys only in the histogram pass: the bounds and
+  // part of that pass overlap the loads still in flight.
+  constexpr bool kEarly = V4 && !STREAM && T == 1024 && VEC >= 2;
+  constexpr int WB = W / 2;
+  bool early = false;
+  if constexpr (kEarly) {
+    early = n >= kEarlyMinFill * SpanT::TILE / 4;
+    if (early) {
+      span.issue(key, 0);
+      if (wid < WB) span.form(key, 0);
+    } else {
+      span.load(key, 0);
+    }
+  } else if constexpr (!STREAM) {
+    span.load(key, 0);
+  }
   auto for_each = [&](auto&& f) { span.template for_each<!STREAM>(key, f); };
 
   hist_clear<T>(sm.sel.hist[0]);
@@ -642,6 +832,20 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
     }
   }
 
+  const uint32_t nm1 = static_cast<uint32_t>(n - 1);
+  int round = 0;
+  // a resident row in float4 layout resolves a key with too many ties by the
+  // positions' prefix counts instead of radix rounds on positions
+  constexpr bool kPrefixTies = V4 && !STREAM;
+  Sel sel{};
+  if constexpr (kEarly) {
+    if (early) {
+      sel = early_round<T, VEC>(span, key, sm.sel, sm.red, k, n);
+      round = 1;
+      sel = refine<T>(for_each, sm.sel, sel, nm1, span.pad_slots(), key[0], round, !kPrefixTies, false);
+    }
+  }
+  if (!early) {
   // ---- bounds: row max and a lower bound of the k-th largest key.  Each
   // thread's jth-largest key, over the nfull threads that hold at least jth
   // scores, gives nfull * jth distinct scores at or above their minimum;
@@ -700,13 +904,8 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
   sel0.bucket = 0xFFFFFFFFu;
 
   // ---- radix refinement until the bucket is small
-  const uint32_t nm1 = static_cast<uint32_t>(n - 1);
-  int round = 0;
-  // a resident row in float4 layout resolves a key with too many ties by the
-  // positions' prefix counts instead of radix rounds on positions
-  constexpr bool kPrefixTies = V4 && !STREAM;
-  const Sel sel = refine<T>(for_each, sm.sel, sel0, nm1, span.pad_slots(), key[0], round,
-                            !kPrefixTies);
+  sel = refine<T>(for_each, sm.sel, sel0, nm1, span.pad_slots(), key[0], round, !kPrefixTies);
+  }
   const bool prefix_ties = kPrefixTies && sel.tie && sel.bucket > static_cast<uint32_t>(kSmallCap);
 
   // ---- scatter: append the bucket to LDS, count the winners, place them by

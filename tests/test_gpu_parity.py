@@ -145,6 +145,27 @@ def test_ties_at_the_lowest_key():
         assert_parity(w, run_gpu(w), run_oracle(w))
 
 
+def test_largest_scores_away_from_the_first_waves():
+    """A row whose largest scores all sit where the last waves of a 1024-lane
+    workgroup read (positions 2048..4095 of every 4096) and whose first
+    waves hold only small ones: the first round's bounds come from the
+    first waves, so the threshold lies in the bin that holds every key above
+    their range."""
+    rng = np.random.default_rng(12)
+    L = 32768
+    x = (rng.standard_normal((4, L)) * 1e-3).astype(np.float32)
+    late = (np.arange(L) % 4096) >= 2048
+    x[0, late] += 100.0
+    x[1, late] = rng.standard_normal(int(late.sum())).astype(np.float32) + 50.0
+    x[2, late & (np.arange(L) % 3 == 0)] = 7.0   # ties above the first waves' range
+    x[3] = -x[3]
+    x[3, late] -= 1.0                              # the late half lowest instead
+    lens = np.array([32768, 30000, 20000, 16384], dtype=np.int32)
+    for k in (1, 1024, 2048):
+        w = _dense("late-max", "raw", x, k, lens)
+        assert_parity(w, run_gpu(w), run_oracle(w))
+
+
 def test_concentrated_rows_small_batch():
     rng = np.random.Generator(np.random.PCG64(9))
     x = np.stack([workloads.concentrated_row(rng, 32768) for _ in range(6)])
