@@ -34,7 +34,7 @@ def _dense(name, api, scores, k, lens=None, ps=64, pt=None):
                     lens=None if lens is None else lens.astype(np.int32))
 
 
-@pytest.mark.parametrize("seed", [42, 43])
+@pytest.mark.parametrize("seed", [42, 43, 44, 45])
 @pytest.mark.parametrize("name", workloads.NAMES)
 def test_named_workloads(name, seed):
     w = workloads.make(name, seed=seed)
