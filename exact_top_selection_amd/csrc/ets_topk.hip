@@ -249,6 +249,45 @@ __device__ __forceinline__ void find_threshold_regs(uint32_t (&h)[kHistBins / T]
   __syncthreads();
 }
 
+// The search of find_threshold_bin by wave 0 alone, one barrier: lane l sums
+// bins [64 l, 64 l + 64); a wave scan from the top finds the lane whose
+// range holds the threshold; that range's 64 bins, one per lane, are scanned
+// the same way.  res[0..2] as find_threshold_bin; the other waves wait at the
+// barrier.
+__device__ __forceinline__ void find_threshold_w0(const uint32_t* hist, uint32_t kk,
+                                                  uint32_t bin0_less, uint32_t* res) {
+  static_assert(kHistBins == 64 * 64, "64 bins per lane");
+  if (threadIdx.x < 64) {
+    const uint32_t l = threadIdx.x;
+    const uint4* q = reinterpret_cast<const uint4*>(hist) + l * 16;
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 v = q[i];
+      sum += (v.x + v.y) + (v.z + v.w);
+    }
+    if (l == 0) sum -= bin0_less;
+    uint32_t incl = wave_incl_scan(sum);
+    const uint32_t total = readlane(incl, 63);
+    uint32_t above = total - incl;  // entries in higher lanes' ranges
+    const uint64_t hit = __ballot(above < kk && kk <= above + sum);
+    const int L = hit ? __ffsll(static_cast<unsigned long long>(hit)) - 1 : 0;
+    const uint32_t base = readlane(above, L);
+    uint32_t h = hist[64 * L + l];
+    if (L == 0 && l == 0) h -= bin0_less;
+    incl = wave_incl_scan(h);
+    above = base + readlane(incl, 63) - incl;
+    const uint64_t hit2 = __ballot(above < kk && kk <= above + h);
+    const int j = hit2 ? __ffsll(static_cast<unsigned long long>(hit2)) - 1 : 0;
+    if (l == static_cast<uint32_t>(j)) {
+      res[0] = 64 * L + j;
+      res[1] = above;
+      res[2] = h;
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- row spans
 
 // key[j] for a lane-varying j, as a binary tree of selects (no scratch).
@@ -405,6 +444,19 @@ struct alignas(16) SelSmem {
   uint32_t res[4];
 };
 
+// The threshold search of a row's round: by wave 0 alone for 1024-lane
+// workgroups (measured faster there: one barrier instead of two, the other
+// 15 waves idle meanwhile), by the whole block for 512 lanes.
+template <int T>
+__device__ __forceinline__ void find_threshold(const uint32_t* hist, uint32_t kk, uint32_t bin0_less,
+                                               SelSmem& sm) {
+  if constexpr (T >= 1024) {
+    find_threshold_w0(hist, kk, bin0_less, sm.res);
+  } else {
+    find_threshold_bin<T>(hist, kk, bin0_less, sm.wsum, sm.res);
+  }
+}
+
 template <int T>
 __device__ __forceinline__ void hist_clear(uint32_t* hist) {
 #pragma unroll
@@ -458,7 +510,7 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
       });
     }
     __syncthreads();
-    find_threshold_bin<T>(hist, kk, rlo == 0 ? n_pad : 0u, sm.wsum, sm.res);
+    find_threshold<T>(hist, kk, rlo == 0 ? n_pad : 0u, sm);
     kk -= sm.res[1];
     bucket = sm.res[2];
     lo = rlo + (sm.res[0] << s);
@@ -480,7 +532,7 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
         if (x == tkey && d <= span) atomicAdd(&hist[d >> s], 1u);
       });
       __syncthreads();
-      find_threshold_bin<T>(hist, kk, 0u, sm.wsum, sm.res);
+      find_threshold<T>(hist, kk, 0u, sm);
       kk -= sm.res[1];
       bucket = sm.res[2];
       dlo = rdlo + (sm.res[0] << s);
@@ -753,7 +805,7 @@ __device__ __forceinline__ Sel early_round(const SpanT& span, uint32_t (&key)[4 
     }
   }
   __syncthreads();
-  find_threshold_bin<T>(hist, static_cast<uint32_t>(k), lo == 0 ? span.pad_slots() : 0u, sm.wsum, sm.res);
+  find_threshold<T>(hist, static_cast<uint32_t>(k), lo == 0 ? span.pad_slots() : 0u, sm);
   Sel out{};
   out.kk = static_cast<uint32_t>(k) - sm.res[1];
   out.bucket = sm.res[2];
@@ -992,10 +1044,12 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
     } else if (!sel.tie) {
       const uint32_t khi = sel.hi, klo = sel.lo, kspan = sel.hi - sel.lo;
       if (klo != 0) {
+        // bucket = at least lo and not a winner
         for_each([&](uint32_t x, int32_t, int) {
           wmask = shift_in_lt(wmask, khi, x);
-          cmask = shift_in_le(cmask, x - klo, kspan);
+          cmask = shift_in_le(cmask, klo, x);
         });
+        cmask &= ~wmask;
       } else {
         for_each([&](uint32_t x, int32_t pos, int) {
           wmask = wmask + wmask + (x > khi ? 1u : 0u);
@@ -1511,11 +1565,13 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     static_assert(PT <= 32, "slot masks are 32 bits");
     if (!sel.tie && sel.lo != 0) {
       // padding (key 0) lies below lo: the plain range tests hold
-      const uint32_t khi = sel.hi, klo = sel.lo, kspan = sel.hi - sel.lo;
+      const uint32_t khi = sel.hi, klo = sel.lo;
+      // bucket = at least lo and not a winner
       for_each([&](uint32_t x, int32_t, int) {
         wmask = shift_in_lt(wmask, khi, x);
-        cmask = shift_in_le(cmask, x - klo, kspan);
+        cmask = shift_in_le(cmask, klo, x);
       });
+      cmask &= ~wmask;
     } else {
       for_each([&](uint32_t x, int32_t pos, int) {
         wmask = wmask + wmask + (sel_winner(sel, nm1, cend, x, pos) ? 1u : 0u);
