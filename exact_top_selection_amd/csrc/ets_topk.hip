@@ -1180,7 +1180,8 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 constexpr int kTieCap = 4096;      // tie-list entries per row
 // Round 0 exchanges 2^kCoarseBits bins per row.  Measured on MI355X for rows
 // of 65536 to 262144 scores: 256 bins beat 64 (larger tie lists) and 1024
-// (more device atomics), and packed bins beat bins spread over more lines.
+// (more device atomics), and packed bins beat bins spread over more lines;
+// 512 bins help N(0,1) rows of 131072 and more but not banded ones.
 constexpr int kCoarseBits = 8;
 constexpr int kCoarseBins = 1 << kCoarseBits;
 constexpr int kFinePerCoarse = kHistBins / kCoarseBins;
@@ -1294,15 +1295,13 @@ __device__ __forceinline__ void clear_bins(uint32_t* buf, uint32_t count) {
 template <int T>
 __device__ __forceinline__ void push_coarse(uint32_t* lh, uint32_t* dst) {
   constexpr int LPC = kFinePerCoarse / 4;  // lanes per coarse bin
-  static_assert(kHistBins / T == 4 && (LPC == 1 || LPC == 4 || LPC == 16), "lanes per coarse bin");
+  static_assert(kHistBins / T == 4 && (LPC == 1 || LPC == 2 || LPC == 4 || LPC == 16), "lanes per coarse bin");
   uint4* q = reinterpret_cast<uint4*>(lh) + threadIdx.x;
   const uint4 c = *q;
   *q = make_uint4(0u, 0u, 0u, 0u);
   uint32_t v = (c.x + c.y) + (c.z + c.w);
-  if constexpr (LPC >= 4) {
-    v += dpp_perm<0xB1>(v);  // quad_perm [1,0,3,2]
-    v += dpp_perm<0x4E>(v);  // quad_perm [2,3,0,1]
-  }
+  if constexpr (LPC >= 2) v += dpp_perm<0xB1>(v);  // quad_perm [1,0,3,2]
+  if constexpr (LPC >= 4) v += dpp_perm<0x4E>(v);  // quad_perm [2,3,0,1]
   if constexpr (LPC >= 16) {
     v += dpp_perm<0x141>(v);  // row_half_mirror
     v += dpp_perm<0x140>(v);  // row_mirror
