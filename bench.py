@@ -63,33 +63,52 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, budget_s: float):
-    """The CPU oracle on the host cores over repeated full batches."""
+    """The CPU oracle on the host cores over repeated full batches, with as
+    many threads as the host offers (at most 16), then on one thread."""
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     oracle.build()
 
-    def once():
+    def once(nt):
         if w.api == "raw":
-            oracle.topk_raw(w.scores, w.k, w.lens, threads=threads)
+            oracle.topk_raw(w.scores, w.k, w.lens, threads=nt)
         elif w.api == "paged":
-            oracle.topk_paged(w.scores, w.lens, w.page_table, w.page_size, w.k, threads=threads)
+            oracle.topk_paged(w.scores, w.lens, w.page_table, w.page_size, w.k, threads=nt)
         else:
-            oracle.topk_ragged(w.scores, w.row_starts, w.lengths, w.k, threads=threads)
+            oracle.topk_ragged(w.scores, w.row_starts, w.lengths, w.k, threads=nt)
 
-    once()  # warm
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        once()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 10000:
-            break
-    rows = reps * w.B
+    def rate(nt, budget):
+        once(nt)  # warm
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            once(nt)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or reps >= 10000:
+                return reps, el
+
+    reps, el = rate(threads, budget_s)
+    reps1, el1 = rate(1, budget_s / 2)
+    rows, rows1 = reps * w.B, reps1 * w.B
     return {"value": rows / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": "%d full batches of %s (%d rows) in %.1f s, %d threads, %s"
-                      % (reps, w.name, rows, el, threads, platform.processor() or platform.machine())}
+            "value_1thread": rows1 / el1,
+            "sample": "%d full batches of %s (%d rows) in %.1f s on %d threads, and %d batches "
+                      "in %.1f s on 1 thread; %s, %d logical CPUs"
+                      % (reps, w.name, rows, el, threads, reps1, el1, cpu_model(),
+                         os.cpu_count() or 0)}
 
 
 COPY_BYTES = 256 << 20
