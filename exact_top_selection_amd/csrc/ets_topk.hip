@@ -1186,13 +1186,13 @@ constexpr int kCoarseBits = 8;
 constexpr int kCoarseBins = 1 << kCoarseBits;
 constexpr int kFinePerCoarse = kHistBins / kCoarseBins;
 constexpr int kGroupPtCap = 1024;  // chunk page-table entries staged in LDS
-constexpr int kRecWords = 64;      // per-row record: its own 256-byte line
+constexpr int kRecWords = 64 + 2 * 64;  // per-row record (a 256-byte line) and one u64 slot per member
 constexpr int kHdrWords = 64;
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 enum HdrField : int { kHdrTicket = 0, kHdrFinished = 16, kHdrError = 32 };
-enum GroupRecField : int { kRecBarrier = 0, kRecDone = 16, kRecCursor = 32 /* u64 */, kRecLb = 56,
-                          kRecHi = 60 };
+enum GroupRecField : int { kRecBarrier = 0, kRecDone = 16, kRecCursor = 32 /* u64 */,
+                          kRecSlots = 64 /* u64 per member */ };
 
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1398,6 +1398,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   const int32_t n = r.n;
   const uint32_t nm1 = static_cast<uint32_t>(n - 1);
   uint32_t* rec = w.rec(b);
+  uint64_t* slots = reinterpret_cast<uint64_t*>(rec + kRecSlots);
   uint32_t* ghist = w.hist(b);
   uint64_t* gties = w.ties(b);
   uint32_t* err = w.hdr + kHdrError;
@@ -1456,15 +1457,43 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
         cmax = max(cmax, sm.sel.wsum[w]);
         clb = min(clb, sm.wsum2[w]);
       }
-      if (nc > 0) max_dev(rec + kRecHi, cmax);
-      if (nfull * jth >= k) max_dev(rec + kRecLb, clb);
+      // one store carries the member's bounds and marks them written:
+      // the high word is the largest key plus one (saturated; 1 for an
+      // empty chunk), never 0
+      const uint32_t hi_enc = nc > 0 ? (cmax == 0xFFFFFFFFu ? cmax : cmax + 1u) : 1u;
+      const uint32_t lbv = nfull * jth >= k ? clb : 0u;
+      st_dev(slots + g, (static_cast<uint64_t>(hi_enc) << 32) | lbv);
     }
   }
-  group_sync(rec + kRecBarrier, static_cast<uint32_t>(G), err);
-  uint32_t nbar = 1;  // group barriers passed
+  // every member's slot, read by the lanes of wave 0: the row's largest key
+  // and the best of the offered lower bounds
+  if (tid < 64) {
+    uint64_t v = 0;
+    if (tid < G) {
+      v = ld_dev(slots + tid);
+      uint32_t spins = 0;
+      while (v == 0) {
+        __builtin_amdgcn_s_sleep(1);
+        v = ld_dev(slots + tid);
+        if (++spins > kSpinLimit) {
+          st_dev(err, 1u);
+          break;
+        }
+      }
+    }
+    const uint32_t he = static_cast<uint32_t>(v >> 32);
+    const uint32_t hi = wave_reduce(he == 0xFFFFFFFFu ? he : (he ? he - 1u : 0u), OpMax());
+    const uint32_t lb = wave_reduce(static_cast<uint32_t>(v), OpMax());
+    if (tid == 0) {
+      sm.base[0] = hi;
+      sm.base[1] = lb;
+    }
+  }
+  __syncthreads();
+  uint32_t nbar = 0;  // group barriers passed
   Sel sel{};
-  sel.lo = ld_dev(rec + kRecLb);
-  sel.hi = ld_dev(rec + kRecHi);
+  sel.lo = sm.base[1];
+  sel.hi = sm.base[0];
   sel.kk = static_cast<uint32_t>(k);
   sel.dlo = 0u;
   sel.dhi = nm1;
@@ -1710,13 +1739,13 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   // its coarse bins; earlier rounds were cleared on the way) and the record
   const int lastr = round - 1;
   clear_bins<T>(ghist + (lastr % 3) * kHistBins, lastr == 0 ? kCoarseBins : kHistBins);
+  // every member has read the slots: it has arrived after its exchange
+  if (tid < G) st_dev(slots + tid, 0ull);
   __syncthreads();  // every wave has read the record before it is reset
   if (tid == 0) {
     st_dev(rec + kRecBarrier, 0u);
     st_dev(rec + kRecDone, 0u);
     st_dev(reinterpret_cast<uint64_t*>(rec + kRecCursor), 0ull);
-    st_dev(rec + kRecLb, 0u);
-    st_dev(rec + kRecHi, 0u);
   }
 }
 

@@ -17,10 +17,11 @@ def dev():
 
 
 # Workspace layout of the row-group path (u32 words): a 64-word header, then
-# per row a 64-word record, three 4096-bin tables and a 4096-entry u64 tie list.
+# per row a 192-word record (counters, then one u64 slot per member), three
+# 4096-bin tables and a 4096-entry u64 tie list.
 WS_HDR = 64
-WS_ROW = 64 + 3 * 4096 + 2 * 4096
-WS_KEPT_ZERO = 64 + 3 * 4096   # record + tables: back at zero after every call
+WS_ROW = 192 + 3 * 4096 + 2 * 4096
+WS_KEPT_ZERO = 192 + 3 * 4096  # record, member slots, tables: back at zero after every call
 
 
 def workspace_dirty(ws: torch.Tensor) -> int:
