@@ -45,6 +45,7 @@ constexpr uint32_t kPeelShare = 16;  // lanes of a wave in one bin that switch t
 // Radix rounds needed at most: 12 + 12 + 8 key bits, then 12 + 12 + 7 position
 // bits; loops stop there even on inconsistent counts, so every kernel ends.
 constexpr int kMaxRounds = 8;
+constexpr int kSubCopies = 4;  // histogram copies of a row's later rounds (lane % 4)
 #ifndef ETS_EARLY_FILL
 #define ETS_EARLY_FILL 2
 #endif
@@ -480,13 +481,21 @@ __device__ __forceinline__ void hist_clear(uint32_t* hist) {
 template <int T, class ForEach>
 __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel in, uint32_t nm1,
                                       uint32_t n_pad, uint32_t probe_key, int& round,
-                                      bool tie_rounds = true, bool above_free = true) {
+                                      bool tie_rounds = true, bool above_free = true,
+                                      uint32_t* sub = nullptr) {
   uint32_t lo = in.lo, hi = in.hi, kk = in.kk, bucket = in.bucket;
   uint32_t tie = 0, dlo = 0, dhi = nm1;
   const int first_round = round;
+  bool sub_clear = false;  // the copies are zero (cleared before their first use)
   while (bucket > static_cast<uint32_t>(kSmallCap) && lo != hi && round < kMaxRounds) {
     uint32_t* hist = sm.hist[round & 1];
     hist_clear<T>(sm.hist[(round + 1) & 1]);
+    if (sub != nullptr && round > 0 && !sub_clear) {
+#pragma unroll
+      for (int c = 0; c < kSubCopies - 1; ++c) hist_clear<T>(sub + c * kHistBins);
+      sub_clear = true;
+      __syncthreads();
+    }
     const uint32_t rlo = lo, span = hi - lo;
     const int bl = span ? 32 - __clz(static_cast<int>(span)) : 0;
     const int s = bl > kHistBits ? bl - kHistBits : 0;
@@ -502,6 +511,18 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
       for_each([&](uint32_t x, int32_t, int) {
         atomicAdd(&hist[min((x - rlo) >> s, dummy)], 1u);
       });
+    } else if (sub != nullptr && round > 0) {
+      // A later round, where a row's keys crowd into few bins: lane l counts
+      // into copy l % kSubCopies of the histogram (copy 0 is hist itself),
+      // so one wave's LDS atomics meet a quarter as many lanes per address;
+      // the copies are merged into hist below.
+      const uint32_t copy = __lane_id() % kSubCopies;
+      uint32_t* base = copy == 0 ? hist : sub + (copy - 1) * kHistBins;
+      uint32_t* dummy = hist + kHistBins + __lane_id();
+      for_each([&](uint32_t x, int32_t, int) {
+        const uint32_t d = x - rlo;
+        atomicAdd(d <= span ? base + (d >> s) : dummy, 1u);
+      });
     } else {
       const uint32_t dummy = kHistBins + __lane_id();
       for_each([&](uint32_t x, int32_t, int) {
@@ -510,6 +531,25 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
       });
     }
     __syncthreads();
+    if (sub != nullptr && round > 0) {
+      // merge the copies into hist and return them to zero (each wave chose
+      // its own path; copies a wave did not touch hold zeros)
+      for (int i = threadIdx.x; i < kHistBins / 4; i += T) {
+        uint4 a = reinterpret_cast<uint4*>(hist)[i];
+#pragma unroll
+        for (int c = 0; c < kSubCopies - 1; ++c) {
+          uint4* q = reinterpret_cast<uint4*>(sub + c * kHistBins) + i;
+          const uint4 b = *q;
+          *q = make_uint4(0u, 0u, 0u, 0u);
+          a.x += b.x;
+          a.y += b.y;
+          a.z += b.z;
+          a.w += b.w;
+        }
+        reinterpret_cast<uint4*>(hist)[i] = a;
+      }
+      __syncthreads();
+    }
     find_threshold<T>(hist, kk, rlo == 0 ? n_pad : 0u, sm);
     kk -= sm.res[1];
     bucket = sm.res[2];
@@ -815,8 +855,11 @@ __device__ __forceinline__ Sel early_round(const SpanT& span, uint32_t (&key)[4 
   return out;
 }
 
+// NSUB histogram copies for later rounds (1024-lane rows; none for 512).
+template <int NSUB>
 struct alignas(16) RowSmem {
   SelSmem sel;
+  uint32_t sub[NSUB > 0 ? NSUB : 1][NSUB > 0 ? kHistBins : 1];  // copies 1.. of a later round's histogram
   int32_t pt[kPtCap];     // staged page-table row (paged map)
   uint2 cand[kSmallCap];  // threshold bucket: (key, position)
   int32_t pos[ETS_MAX_K]; // selected positions by output slot
@@ -828,7 +871,8 @@ struct alignas(16) RowSmem {
 // tile) is loaded once and every pass runs on registers.  STREAM = true: any
 // length; every pass streams the row tile by tile (L2 after the first).
 template <int T, int VEC, int MODE, bool V4, bool STREAM>
-__device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const RowRef<MODE>& r) {
+__device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kSubCopies - 1 : 0>& sm,
+                                         const RowRef<MODE>& r) {
   using SpanT = Span<T, VEC, V4>;
   constexpr int PT = SpanT::PT;
   constexpr int W = T / 64;
@@ -894,7 +938,8 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
     if (early) {
       sel = early_round<T, VEC>(span, key, sm.sel, sm.red, k, n);
       round = 1;
-      sel = refine<T>(for_each, sm.sel, sel, nm1, span.pad_slots(), key[0], round, !kPrefixTies, false);
+      sel = refine<T>(for_each, sm.sel, sel, nm1, span.pad_slots(), key[0], round, !kPrefixTies, false,
+                      T >= 1024 ? &sm.sub[0][0] : nullptr);
     }
   }
   if (!early) {
@@ -956,7 +1001,8 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
   sel0.bucket = 0xFFFFFFFFu;
 
   // ---- radix refinement until the bucket is small
-  sel = refine<T>(for_each, sm.sel, sel0, nm1, span.pad_slots(), key[0], round, !kPrefixTies);
+  sel = refine<T>(for_each, sm.sel, sel0, nm1, span.pad_slots(), key[0], round, !kPrefixTies, true,
+                  T >= 1024 ? &sm.sub[0][0] : nullptr);
   }
   const bool prefix_ties = kPrefixTies && sel.tie && sel.bucket > static_cast<uint32_t>(kSmallCap);
 
@@ -1117,7 +1163,7 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem& sm, const Row
 template <int T, int VEC, int MODE, bool V4, bool STREAM>
 __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
   constexpr int TILE = T * 4 * VEC;
-  __shared__ RowSmem sm;
+  __shared__ RowSmem<T >= 1024 ? kSubCopies - 1 : 0> sm;
   const RowRef<MODE> r(p, blockIdx.x);
   if (r.n <= p.k) {
     emit_whole_row<T, MODE>(p, r);
