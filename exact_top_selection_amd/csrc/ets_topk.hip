@@ -46,6 +46,8 @@ constexpr uint32_t kPeelShare = 16;  // lanes of a wave in one bin that switch t
 // bits; loops stop there even on inconsistent counts, so every kernel ends.
 constexpr int kMaxRounds = 8;
 constexpr int kSubCopies = 4;  // histogram copies of a row's later rounds (lane % 4)
+// words between copies: a bin of two copies falls in different LDS banks
+constexpr int kSubStride = (1 << 12) + 8;
 #ifndef ETS_EARLY_FILL
 #define ETS_EARLY_FILL 2
 #endif
@@ -492,7 +494,7 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
     hist_clear<T>(sm.hist[(round + 1) & 1]);
     if (sub != nullptr && round > 0 && !sub_clear) {
 #pragma unroll
-      for (int c = 0; c < kSubCopies - 1; ++c) hist_clear<T>(sub + c * kHistBins);
+      for (int c = 0; c < kSubCopies; ++c) hist_clear<T>(sub + c * kSubStride);
       sub_clear = true;
       __syncthreads();
     }
@@ -513,11 +515,10 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
       });
     } else if (sub != nullptr && round > 0) {
       // A later round, where a row's keys crowd into few bins: lane l counts
-      // into copy l % kSubCopies of the histogram (copy 0 is hist itself),
-      // so one wave's LDS atomics meet a quarter as many lanes per address;
-      // the copies are merged into hist below.
-      const uint32_t copy = __lane_id() % kSubCopies;
-      uint32_t* base = copy == 0 ? hist : sub + (copy - 1) * kHistBins;
+      // into copy l % kSubCopies of the histogram, so one wave's LDS atomics
+      // meet a quarter as many lanes per address and bank; the copies are
+      // merged into hist below.
+      uint32_t* base = sub + (__lane_id() % kSubCopies) * kSubStride;
       uint32_t* dummy = hist + kHistBins + __lane_id();
       for_each([&](uint32_t x, int32_t, int) {
         const uint32_t d = x - rlo;
@@ -537,8 +538,8 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
       for (int i = threadIdx.x; i < kHistBins / 4; i += T) {
         uint4 a = reinterpret_cast<uint4*>(hist)[i];
 #pragma unroll
-        for (int c = 0; c < kSubCopies - 1; ++c) {
-          uint4* q = reinterpret_cast<uint4*>(sub + c * kHistBins) + i;
+        for (int c = 0; c < kSubCopies; ++c) {
+          uint4* q = reinterpret_cast<uint4*>(sub + c * kSubStride) + i;
           const uint4 b = *q;
           *q = make_uint4(0u, 0u, 0u, 0u);
           a.x += b.x;
@@ -859,7 +860,7 @@ __device__ __forceinline__ Sel early_round(const SpanT& span, uint32_t (&key)[4 
 template <int NSUB>
 struct alignas(16) RowSmem {
   SelSmem sel;
-  uint32_t sub[NSUB > 0 ? NSUB : 1][NSUB > 0 ? kHistBins : 1];  // copies 1.. of a later round's histogram
+  uint32_t sub[NSUB > 0 ? NSUB : 1][NSUB > 0 ? kSubStride : 1];  // a later round's histogram copies
   int32_t pt[kPtCap];     // staged page-table row (paged map)
   uint2 cand[kSmallCap];  // threshold bucket: (key, position)
   int32_t pos[ETS_MAX_K]; // selected positions by output slot
@@ -871,7 +872,7 @@ struct alignas(16) RowSmem {
 // tile) is loaded once and every pass runs on registers.  STREAM = true: any
 // length; every pass streams the row tile by tile (L2 after the first).
 template <int T, int VEC, int MODE, bool V4, bool STREAM>
-__device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kSubCopies - 1 : 0>& sm,
+__device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kSubCopies : 0>& sm,
                                          const RowRef<MODE>& r) {
   using SpanT = Span<T, VEC, V4>;
   constexpr int PT = SpanT::PT;
@@ -1163,7 +1164,7 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kS
 template <int T, int VEC, int MODE, bool V4, bool STREAM>
 __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
   constexpr int TILE = T * 4 * VEC;
-  __shared__ RowSmem<T >= 1024 ? kSubCopies - 1 : 0> sm;
+  __shared__ RowSmem<T >= 1024 ? kSubCopies : 0> sm;
   const RowRef<MODE> r(p, blockIdx.x);
   if (r.n <= p.k) {
     emit_whole_row<T, MODE>(p, r);
