@@ -1190,29 +1190,32 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // method's rounds together inside one launch (the pages' row-split path,
 // PR #37591 topk.hip excerpt, carries each row's histogram through a
 // workspace between separate kernels; here the kernel boundaries are
-// replaced by waits on per-row counters):
+// replaced by waits inside the kernel):
 //
-//  * round 0: every workgroup builds an LDS histogram of its chunk on the
-//    key's top 12 bits and adds the bins at or above its own chunk's
-//    threshold bin into the row's histogram.  The row's k-th largest key is
-//    at least any chunk's min(k, chunk)-th largest, so a bin below a chunk's
-//    threshold bin never holds the row's threshold and is not needed;
-//  * after the group's barrier every workgroup reads the row histogram and
-//    finds the same threshold bin.  A bucket larger than the tie list
-//    (scores concentrated in a few bins) is narrowed by further rounds of
-//    12-bit digits of the key, then of the position among equal keys;
-//  * every workgroup writes its winners to the output and appends its
-//    bucket members to the row's tie list, both placed through one 64-bit
-//    cursor;
-//  * the last workgroup of the group to finish ranks the tie list exactly
+//  * bounds: every member stores its chunk's largest key and a lower bound
+//    of the row's k-th largest (from its lanes' jth-largest keys) in its own
+//    slot, one 64-bit store that also marks the slot written; the members
+//    poll the row's G slots and take the largest key and the best bound;
+//  * round 0: every member builds a 12-bit LDS histogram of its chunk over
+//    [lower bound, largest key], merges 16 fine bins to one and adds the
+//    256 coarse bins into the row's table; after the group's barrier every
+//    wave reads the coarse table and finds the same threshold bin.  A bucket
+//    larger than the tie list (scores concentrated in a few bins) is
+//    narrowed by further rounds of 12-bit digits of the key, then of the
+//    position among equal keys;
+//  * every member writes its winners to the output and appends its bucket
+//    members to the row's tie list, both placed through one 64-bit cursor;
+//  * the last member of the group to finish ranks the tie list exactly
 //    (LDS radix rounds, then direct comparison), emits the rest of the row
 //    and returns the row's workspace to zero.
 //
-// Groups are formed in the order workgroups start (a ticket counter), so a
-// workgroup only ever waits for members that have started or start next:
-// progress needs room for one group on the device, not for the whole grid.
-// Every wait is bounded; on expiry the workspace's error word is set, the
-// call's output is undefined, and the kernel still ends.
+// Workgroup i is member i % G of row i / G when the whole grid fits the
+// device at once; otherwise groups are formed in the order workgroups start
+// (a ticket counter), so that a workgroup only ever waits for members that
+// have started or start next and progress needs room for one group on the
+// device, not for the whole grid.  Every wait is bounded; on expiry the
+// workspace's error word is set, the call's output is undefined, and the
+// kernel still ends.
 //
 // Data crosses workgroups only through device-scope relaxed atomics (loads
 // and stores are issued coherent at device scope, read-modify-writes are
@@ -1220,9 +1223,10 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // before an arrival is counted, so no cache write-back or invalidate is
 // needed.
 //
-// Workspace (u32 words): hdr[64], then per row rec[64] | hist[3][4096] | ties[kTieCap] (u64).
-// It must be zero before its first use; every call returns the header, the
-// records and the tables to zero (tie lists may keep stale entries).
+// Workspace (u32 words): hdr[64], then per row rec[192] (counters, then one
+// u64 slot per member) | hist[3][4096] | ties[kTieCap] (u64).  It must be
+// zero before its first use; every call returns the header, the records and
+// the tables to zero (tie lists may keep stale entries).
 
 constexpr int kTieCap = 4096;      // tie-list entries per row
 // Round 0 exchanges 2^kCoarseBits bins per row.  Measured on MI355X for rows
