@@ -263,10 +263,14 @@ __device__ __forceinline__ void find_threshold_w0(const uint32_t* hist, uint32_t
   if (threadIdx.x < 64) {
     const uint32_t l = threadIdx.x;
     const uint4* q = reinterpret_cast<const uint4*>(hist) + l * 16;
+    // lanes 256 bytes apart would all meet the same banks: lane l visits its
+    // 16-byte groups in the order i ^ (l % 16), so the lanes that the LDS
+    // serves together read different banks
+    const uint32_t rot = l & 15u;
     uint32_t sum = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint4 v = q[i];
+      const uint4 v = q[static_cast<uint32_t>(i) ^ rot];
       sum += (v.x + v.y) + (v.z + v.w);
     }
     if (l == 0) sum -= bin0_less;
