@@ -642,41 +642,45 @@ __device__ __forceinline__ int32_t out_value(const Params& p, bool use_lds, cons
   }
 }
 
+// A bucket entry: key and position as one 64-bit word, (key << 32) |
+// ~position, whose unsigned order is the order on (key desc, position asc).
+// A zero word is no entry: it ranks below every entry.
+__device__ __forceinline__ uint64_t bucket_entry(uint32_t key, int32_t pos) {
+  return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(pos));
+}
+
 // Ranks up to kSmallCap bucket entries on (key desc, position asc) and emits
 // the kk best at slots first + rank.  G = T / kSmallCap lanes share an entry:
 // each compares it with every G-th entry, then row permutes sum the G counts.
-// (key, ~position) as one 64-bit word orders the entries the same way.
+// cand holds the nc entries followed by zero words up to kSmallCap, so no
+// read is clamped and no comparison tests an index.
 template <int T, class Emit>
-__device__ __forceinline__ void rank_bucket(const uint2* cand, uint32_t nc, uint32_t kk,
+__device__ __forceinline__ void rank_bucket(const uint64_t* cand, uint32_t nc, uint32_t kk,
                                             uint32_t first, Emit&& emit) {
   constexpr int G = T / kSmallCap;
   static_assert(G == 2 || G == 4 || G == 8, "2, 4 or 8 lanes per bucket entry");
   constexpr int Q = kSmallCap / G;  // entries compared by each lane
   constexpr int QB = 4;             // entries read per batch: small buckets read little
+  static_assert(Q % QB == 0, "whole batches");
   const uint32_t i = threadIdx.x / G;
   const uint32_t part = threadIdx.x % G;
   // a wave whose entries all lie past the bucket has nothing to rank
   if ((threadIdx.x & ~63u) / G >= nc) return;
-  const uint32_t last = nc > 0 ? nc - 1 : 0;
-  const uint2 ci = cand[min(i, last)];
-  const uint64_t vi = (static_cast<uint64_t>(ci.x) << 32) | static_cast<uint32_t>(~ci.y);
+  const uint64_t vi = cand[i];
   uint32_t rank = 0;
 #pragma unroll
   for (int q0 = 0; q0 < Q; q0 += QB) {
     if (static_cast<uint32_t>(G * q0) >= nc) break;
-    uint2 cj[QB];
+    uint64_t vj[QB];
 #pragma unroll
-    for (int q = 0; q < QB; ++q) cj[q] = cand[min(part + G * (q0 + q), last)];
+    for (int q = 0; q < QB; ++q) vj[q] = cand[part + G * (q0 + q)];
 #pragma unroll
-    for (int q = 0; q < QB; ++q) {
-      const uint64_t vj = (static_cast<uint64_t>(cj[q].x) << 32) | static_cast<uint32_t>(~cj[q].y);
-      rank += static_cast<uint32_t>((part + G * (q0 + q) < nc) & (vj > vi));
-    }
+    for (int q = 0; q < QB; ++q) rank += vj[q] > vi ? 1u : 0u;
   }
   rank += dpp_perm<0xB1>(rank);                         // quad_perm [1,0,3,2]: pairs
   if constexpr (G >= 4) rank += dpp_perm<0x4E>(rank);   // quad_perm [2,3,0,1]: quads
   if constexpr (G >= 8) rank += dpp_perm<0x141>(rank);  // row_half_mirror: eights
-  if (i < nc && part == 0 && rank < kk) emit(first + rank, static_cast<int32_t>(ci.y));
+  if (i < nc && part == 0 && rank < kk) emit(first + rank, static_cast<int32_t>(~static_cast<uint32_t>(vi)));
 }
 
 // Row geometry shared by every kernel: valid length, base pointer, offsets.
@@ -866,7 +870,7 @@ struct alignas(16) RowSmem {
   SelSmem sel;
   uint32_t sub[NSUB > 0 ? NSUB : 1][NSUB > 0 ? kSubStride : 1];  // a later round's histogram copies
   int32_t pt[kPtCap];     // staged page-table row (paged map)
-  uint2 cand[kSmallCap];  // threshold bucket: (key, position)
+  uint64_t cand[kSmallCap];  // threshold bucket (bucket_entry words, zero past the bucket)
   int32_t pos[ETS_MAX_K]; // selected positions by output slot
   uint32_t red[64];       // per-wave partials (bounds)
   uint32_t ccount;
@@ -925,6 +929,7 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kS
 
   hist_clear<T>(sm.sel.hist[0]);
   if (tid == 0) sm.ccount = 0;
+  if (tid < kSmallCap) sm.cand[tid] = 0ull;
   if constexpr (MODE == kPaged) {
     if (pt_lds) {
 #pragma unroll
@@ -1032,7 +1037,7 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kS
   };
   auto append = [&](uint32_t x, int32_t pos) {
     const uint32_t slot = atomicAdd(&sm.ccount, 1u);
-    if (slot < static_cast<uint32_t>(kSmallCap)) sm.cand[slot] = make_uint2(x, static_cast<uint32_t>(pos));
+    if (slot < static_cast<uint32_t>(kSmallCap)) sm.cand[slot] = bucket_entry(x, pos);
   };
   if constexpr (!STREAM) {
     // bit PT-1-j of wmask / cmask: slot j is a winner / in the bucket
@@ -1428,7 +1433,7 @@ __device__ __forceinline__ void narrow(Sel& sel, const uint32_t* res, int s) {
 struct alignas(16) GroupSmem {
   SelSmem sel;              // histograms (hist[0] is zero between rounds) and scan scratch
   int32_t pt[kGroupPtCap];  // the chunk's page-table entries (paged map)
-  uint2 cand[kSmallCap];    // final bucket of the tie list
+  uint64_t cand[kSmallCap];  // final bucket of the tie list (bucket_entry words, zero past it)
   union {
     int32_t pos[ETS_MAX_K];  // this workgroup's winners, in slot order
     uint2 ties[kTieCap];     // the last workgroup: the row's tie list
@@ -1759,6 +1764,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     sm.wcount = 0;
     sm.ccount = 0;
   }
+  if (tid < kSmallCap) sm.cand[tid] = 0ull;
   __syncthreads();
   const int trips = static_cast<int>((m + T - 1) / T);
   const uint32_t tpad = static_cast<uint32_t>(trips) * T - m;
@@ -1783,7 +1789,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
       if (slot < first2) r.out[slot] = map_any(pos);
     } else if (sel_bucket(fin, nm1, n, x, pos)) {
       const uint32_t c = atomicAdd(&sm.ccount, 1u);
-      if (c < static_cast<uint32_t>(kSmallCap)) sm.cand[c] = make_uint2(x, static_cast<uint32_t>(pos));
+      if (c < static_cast<uint32_t>(kSmallCap)) sm.cand[c] = bucket_entry(x, pos);
     }
   });
   __syncthreads();
