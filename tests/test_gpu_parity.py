@@ -145,6 +145,28 @@ def test_ties_at_the_lowest_key():
         assert_parity(w, run_gpu(w), run_oracle(w))
 
 
+@pytest.mark.parametrize("copies", [1, 2, 64, 127, 128, 129, 200])
+def test_threshold_key_with_copies(copies):
+    """The k-th largest score repeated `copies` times at random positions, with
+    k - copies // 2 larger scores: the kernel takes the lowest-position half of
+    the copies.  Copies of at most 128 are ranked directly (entries ordered by
+    key, then position); more go through the tie rounds.  Rows that fit one
+    workgroup and rows split over a row group."""
+    rng = np.random.default_rng(1000 + copies)
+    for L, lens in ((32768, [32768, 20000, 8192]), (70001, [70001, 40000])):
+        B = len(lens)
+        x = (rng.standard_normal((B, L)) - 4.0).astype(np.float32)  # below the copies
+        for k in (1024, 2048):
+            y = x.copy()
+            for b, n in enumerate(lens):
+                pos = rng.permutation(n)
+                above = k - copies // 2
+                y[b, pos[:above]] = (rng.random(above) + 2.0).astype(np.float32)
+                y[b, pos[above:above + copies]] = np.float32(1.5)
+            w = _dense("copies", "raw", y, k, np.array(lens, dtype=np.int32))
+            assert_parity(w, run_gpu(w), run_oracle(w))
+
+
 def test_largest_scores_away_from_the_first_waves():
     """A row whose largest scores all sit where the last waves of a 1024-lane
     workgroup read (positions 2048..4095 of every 4096) and whose first
