@@ -1207,8 +1207,11 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 //    poll the row's G slots and take the largest key and the best bound;
 //  * round 0: every member builds a 12-bit LDS histogram of its chunk over
 //    [lower bound, largest key], merges 16 fine bins to one and adds the
-//    256 coarse bins into the row's table; after the group's barrier every
-//    wave reads the coarse table and finds the same threshold bin.  A bucket
+//    256 coarse bins into the row's table, and the count of its scores
+//    under the lower bound into one more word; one wave of every member
+//    polls the table until it and that word hold all n scores of the row
+//    (no barrier: the total reaches n only once every member's adds have
+//    landed) and finds the same threshold bin.  A bucket
 //    larger than the tie list (scores concentrated in a few bins) is
 //    narrowed by further rounds of 12-bit digits of the key, then of the
 //    position among equal keys;
@@ -1229,7 +1232,8 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // Data crosses workgroups only through device-scope relaxed atomics (loads
 // and stores are issued coherent at device scope, read-modify-writes are
 // performed in the memory hierarchy), with each wave's memory counter drained
-// before an arrival is counted, so no cache write-back or invalidate is
+// before an arrival is counted (or, for the coarse table, completion read
+// from the table's own total), so no cache write-back or invalidate is
 // needed.
 //
 // Workspace (u32 words): hdr[64], then per row rec[192] (counters, then one
@@ -1252,7 +1256,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 
 enum HdrField : int { kHdrTicket = 0, kHdrFinished = 16, kHdrError = 32 };
 enum GroupRecField : int { kRecBarrier = 0, kRecDone = 16, kRecCursor = 32 /* u64 */,
-                          kRecSlots = 64 /* u64 per member */ };
+                          kRecBelow = 48, kRecSlots = 64 /* u64 per member */ };
 
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1352,14 +1356,16 @@ __device__ __forceinline__ void clear_bins(uint32_t* buf, uint32_t count) {
 
 // Adds the LDS histogram, merged kFinePerCoarse bins at a time, into the
 // coarse table dst (device atomics; zero bins are skipped) and clears it.
+// Returns the count of the calling thread's four bins.
 template <int T>
-__device__ __forceinline__ void push_coarse(uint32_t* lh, uint32_t* dst) {
+__device__ __forceinline__ uint32_t push_coarse(uint32_t* lh, uint32_t* dst) {
   constexpr int LPC = kFinePerCoarse / 4;  // lanes per coarse bin
   static_assert(kHistBins / T == 4 && (LPC == 1 || LPC == 2 || LPC == 4 || LPC == 16), "lanes per coarse bin");
   uint4* q = reinterpret_cast<uint4*>(lh) + threadIdx.x;
   const uint4 c = *q;
   *q = make_uint4(0u, 0u, 0u, 0u);
-  uint32_t v = (c.x + c.y) + (c.z + c.w);
+  const uint32_t own = (c.x + c.y) + (c.z + c.w);
+  uint32_t v = own;
   if constexpr (LPC >= 2) v += dpp_perm<0xB1>(v);  // quad_perm [1,0,3,2]
   if constexpr (LPC >= 4) v += dpp_perm<0x4E>(v);  // quad_perm [2,3,0,1]
   if constexpr (LPC >= 16) {
@@ -1367,28 +1373,46 @@ __device__ __forceinline__ void push_coarse(uint32_t* lh, uint32_t* dst) {
     v += dpp_perm<0x140>(v);  // row_mirror
   }
   if ((threadIdx.x % LPC) == 0 && v != 0) add_dev(dst + threadIdx.x / LPC, v);
+  return own;
 }
 
-// Every wave reads the coarse table src and finds its threshold bin for kk:
-// (bin, entries above it, entries in it), the same in every lane.  No barrier.
-__device__ __forceinline__ uint3 find_coarse(const uint32_t* src, uint32_t kk) {
+// One wave polls the row's coarse table src, and the count below of the
+// row's scores under the round's range, until together they hold all n
+// scores: each member adds its bins and its count under the range, every
+// word only grows, so the total reaches n exactly when every member's adds
+// have landed, and then every word is final.  Then finds the threshold bin
+// for kk: (bin, entries above it, entries in it), the same in every lane.  A
+// wait past kSpinLimit polls sets the error flag and returns what it read.
+__device__ __forceinline__ uint3 poll_coarse(const uint32_t* src, const uint32_t* below, uint32_t n,
+                                             uint32_t kk, uint32_t* err) {
   constexpr int C = kCoarseBins / 64;  // coarse bins per lane
   static_assert(C * 64 == kCoarseBins && (C == 1 || C % 2 == 0), "coarse bins per lane");
   const uint32_t l = __lane_id();
   uint32_t h[C];
-  if constexpr (C >= 2) {
-#pragma unroll
-    for (int i = 0; i < C; i += 2) {
-      const uint64_t a = ld_dev(reinterpret_cast<const uint64_t*>(src + C * l + i));
-      h[i] = static_cast<uint32_t>(a);
-      h[i + 1] = static_cast<uint32_t>(a >> 32);
-    }
-  } else {
-    h[0] = ld_dev(src + l);
-  }
   uint32_t sum = 0;
+  for (uint32_t spins = 0;; ++spins) {
+    if constexpr (C >= 2) {
 #pragma unroll
-  for (int i = 0; i < C; ++i) sum += h[i];
+      for (int i = 0; i < C; i += 2) {
+        const uint64_t a = ld_dev(reinterpret_cast<const uint64_t*>(src + C * l + i));
+        h[i] = static_cast<uint32_t>(a);
+        h[i + 1] = static_cast<uint32_t>(a >> 32);
+      }
+    } else {
+      h[0] = ld_dev(src + l);
+    }
+    const uint32_t b = __builtin_amdgcn_readfirstlane(ld_dev(below));
+    sum = 0;
+#pragma unroll
+    for (int i = 0; i < C; ++i) sum += h[i];
+    const uint32_t total = wave_reduce(sum, OpAdd()) + b;
+    if (total == n) break;
+    if (spins > kSpinLimit) {
+      if (l == 0) st_dev(err, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
   const uint32_t incl = wave_incl_scan(sum);
   uint32_t above = readlane(incl, 63) - incl;  // entries in higher lanes' bins
   uint32_t t = 0, ta = 0, th = 0;
@@ -1583,12 +1607,30 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     __syncthreads();
   }
   // the row's histogram, 16 bins to one: few device atomics per member, and a
-  // coarse threshold bucket that the tie list absorbs
-  push_coarse<T>(lh, ghist);
-  group_sync(rec + kRecBarrier, static_cast<uint32_t>(G) * ++nbar, err);
+  // coarse threshold bucket that the tie list absorbs; with it the count of
+  // the chunk's scores under lo, so that the table tells when it is whole
   {
-    const uint3 c = find_coarse(ghist, sel.kk);
-    const uint32_t res[3] = {c.x, c.y, c.z};
+    const uint32_t win = wave_reduce(push_coarse<T>(lh, ghist), OpAdd());
+    if (__lane_id() == 0) sm.wsum2[wid] = win;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t in_range = 0;
+    for (int w = 0; w < W; ++w) in_range += sm.wsum2[w];
+    const uint32_t under = static_cast<uint32_t>(nc) - in_range;
+    if (under != 0) add_dev(rec + kRecBelow, under);
+  }
+  if (tid < 64) {
+    const uint3 c = poll_coarse(ghist, rec + kRecBelow, static_cast<uint32_t>(n), sel.kk, err);
+    if (tid == 0) {
+      sm.sel.res[0] = c.x;
+      sm.sel.res[1] = c.y;
+      sm.sel.res[2] = c.z;
+    }
+  }
+  __syncthreads();
+  {
+    const uint32_t res[3] = {sm.sel.res[0], sm.sel.res[1], sm.sel.res[2]};
     narrow(sel, res, s0 + (kHistBits - kCoarseBits));
   }
 
@@ -1806,6 +1848,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   if (tid == 0) {
     st_dev(rec + kRecBarrier, 0u);
     st_dev(rec + kRecDone, 0u);
+    st_dev(rec + kRecBelow, 0u);
     st_dev(reinterpret_cast<uint64_t*>(rec + kRecCursor), 0ull);
   }
 }
