@@ -1991,7 +1991,7 @@ constexpr int64_t kRowTile = static_cast<int64_t>(kRowThreads) * 4 * kRowVec;
 
 // row-group path: 1024-lane workgroups, each holding up to VEC float4 per lane
 constexpr int kGroupThreads = 1024;
-constexpr int64_t kGroupChunk = 8192;  // scores per workgroup of a split row
+constexpr int64_t kGroupChunk = 16384;  // scores per workgroup of a split row
 constexpr int64_t kMaxGroup = 64;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
@@ -2000,11 +2000,14 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 // that fits one resident 32768-score tile stays on one workgroup: measured on
 // MI355X, the group's exchanges cost more than the work they spread.  Longer
 // rows are cut into chunks of about kGroupChunk scores, at most kMaxGroup per
-// row.  ETS_ROW_SPLIT overrides: 0 or 1 = one workgroup per row, n >= 2 = n
-// workgroups per row (at most kMaxGroup).  The compute-unit count is part of
-// the interface for heuristics that weigh it; this one does not need it.
+// row, and the whole grid is held to two workgroups per compute unit: a sweep
+// of B in 1..256, row lengths 65536..262144 and 2..64 workgroups per row put
+// the best chunk at 16384 scores while B * G <= 2 * CUs, and one workgroup per
+// row ahead once fewer than four workgroups per row fit that bound (the rows
+// alone then keep every compute unit busy).  cu_count <= 0 (unknown) lifts the
+// bound.  ETS_ROW_SPLIT overrides: 0 or 1 = one workgroup per row, n >= 2 = n
+// workgroups per row (at most kMaxGroup).
 int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count) {
-  (void)cu_count;
   if (B <= 0 || max_len <= 0) return 0;
   if (const char* e = std::getenv("ETS_ROW_SPLIT"); e != nullptr && *e != '\0') {
     char* end = nullptr;
@@ -2015,7 +2018,13 @@ int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count) {
     }
   }
   if (max_len <= kRowTile) return 0;
-  return static_cast<int32_t>(std::min((max_len + kGroupChunk - 1) / kGroupChunk, kMaxGroup));
+  int64_t G = std::min((max_len + kGroupChunk - 1) / kGroupChunk, kMaxGroup);
+  if (cu_count > 0) {
+    const int64_t fit = 2 * static_cast<int64_t>(cu_count) / B;  // workgroups per row in 2 * CUs
+    if (fit < 4) return 0;
+    G = std::min(G, fit);
+  }
+  return static_cast<int32_t>(G);
 }
 
 size_t group_ws_bytes(int32_t B) {

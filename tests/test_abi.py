@@ -130,15 +130,26 @@ def test_row_split_heuristic():
         # rows that fit one 32768-score workgroup tile stay whole, whatever the batch
         for B, L in ((64, 32768), (128, 32768), (48, 8192), (1, 2048), (4, 4096), (1024, 8192)):
             assert ets.row_split(B, L, 256) == 0, (B, L)
-        # longer rows are cut into chunks of about 8192 scores, at most 64
-        assert ets.row_split(4, 32769, 256) == 5
-        assert ets.row_split(4, 65536, 256) == 8
-        assert ets.row_split(2, 100000, 256) == 13
-        assert ets.row_split(4, 262144, 256) == 32
-        assert ets.row_split(4096, 262144, 256) == 32
+        # longer rows are cut into chunks of about 16384 scores, at most 64
+        assert ets.row_split(4, 32769, 256) == 3
+        assert ets.row_split(4, 65536, 256) == 4
+        assert ets.row_split(2, 100000, 256) == 7
+        assert ets.row_split(4, 262144, 256) == 16
+        assert ets.row_split(16, 262144, 256) == 16
         assert ets.row_split(1, 10 ** 7, 256) == 64
         assert ets.row_split(0, 262144, 256) == 0
-        assert ets.row_split(4, 262144, 0) == 32
+        # the grid is held to two workgroups per compute unit ...
+        assert ets.row_split(64, 262144, 256) == 8
+        assert ets.row_split(64, 65536, 256) == 4
+        assert ets.row_split(128, 262144, 256) == 4
+        assert ets.row_split(64, 10 ** 7, 256) == 8
+        # ... and rows stay whole once fewer than four per row fit it
+        assert ets.row_split(129, 262144, 256) == 0
+        assert ets.row_split(256, 65536, 256) == 0
+        assert ets.row_split(4096, 262144, 256) == 0
+        # an unknown compute-unit count lifts the bound
+        assert ets.row_split(4, 262144, 0) == 16
+        assert ets.row_split(4096, 262144, 0) == 16
     finally:
         if env is not None:
             os.environ["ETS_ROW_SPLIT"] = env

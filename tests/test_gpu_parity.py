@@ -315,3 +315,35 @@ def test_ragged_hint_below_row_length(hint):
                               torch.from_numpy(lengths).to(d), k, max_len=hint)
         torch.cuda.synchronize()
         assert_parity(w, out.cpu().numpy(), run_oracle(w))
+
+
+@pytest.mark.parametrize("overlap", [False, True])
+def test_variable_windows(overlap):
+    """Per-row windows inside dense rows through the ragged call: row b reads
+    [row_starts[b], row_starts[b] + lengths[b]) of the flat score buffer and
+    its indices are absolute.  Overlapping windows (sliding windows over one
+    sequence, as in decode) read shared scores; long windows take the row-group
+    path."""
+    rng = np.random.default_rng(2024 + overlap)
+    if overlap:
+        B = 4
+        lengths = np.array([70001, 120000, 262144, 99999], dtype=np.int32)
+        starts = (np.arange(B, dtype=np.int64) * 3001 + 7).astype(np.int32)
+        total = int((starts.astype(np.int64) + lengths).max())
+        flat = rng.standard_normal(total).astype(np.float32)
+    else:
+        B, L = 6, 40000
+        offs = rng.integers(0, L, B)
+        offs[0] = 0
+        lengths = np.array([rng.integers(0, L - o + 1) for o in offs], dtype=np.int32)
+        lengths[1] = L - offs[1]
+        starts = (np.arange(B) * L + offs).astype(np.int32)
+        flat = rng.standard_normal(B * L).astype(np.float32)
+    d = dev()
+    for k in (1, 1024, 2048):
+        print("case windows overlap", overlap, "k", k, flush=True)
+        w = Workload("windows", "ragged", k, B, flat, row_starts=starts, lengths=lengths)
+        out = ets.topk_ragged(torch.from_numpy(flat).to(d), torch.from_numpy(starts).to(d),
+                              torch.from_numpy(lengths).to(d), k, max_len=int(lengths.max()))
+        torch.cuda.synchronize()
+        assert_parity(w, out.cpu().numpy(), run_oracle(w))
