@@ -1992,7 +1992,9 @@ constexpr int64_t kRowTile = static_cast<int64_t>(kRowThreads) * 4 * kRowVec;
 // row-group path: 1024-lane workgroups, each holding up to VEC float4 per lane
 constexpr int kGroupThreads = 1024;
 constexpr int64_t kGroupChunk = 16384;  // scores per workgroup of a split row
-constexpr int64_t kMaxGroup = 64;
+// 64 members per row tripped the bounded waits (error word set) on grids of
+// 4096 or more workgroups, for a cause not yet found; 32 never did.
+constexpr int64_t kMaxGroup = 32;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 

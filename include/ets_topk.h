@@ -141,12 +141,12 @@ ets_status ets_workspace_init(void* workspace, size_t bytes, void* stream);
  * Workgroups per row the library uses for (B, max_row_len) on a device with
  * `cu_count` compute units; 0 means one workgroup per row.  Pure host
  * function.  Rows that fit one workgroup's 32768-score tile stay whole;
- * longer rows are cut into chunks of about 16384 scores, at most 64 per row,
+ * longer rows are cut into chunks of about 16384 scores, at most 32 per row,
  * with B * G held to 2 * cu_count; where that leaves fewer than 4 per row,
  * rows stay whole (cu_count <= 0 lifts that bound).
  * The environment variable ETS_ROW_SPLIT, when set to an integer >= 0,
  * overrides the heuristic (0 or 1: one workgroup per row; n: n workgroups per
- * row, at most 64).  After the pages' row_split heuristic (PR #37591 digest,
+ * row, at most 32).  After the pages' row_split heuristic (PR #37591 digest,
  * the topk.hip excerpt), with constants of this library measured on MI355X.
  */
 int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count);

@@ -120,7 +120,7 @@ def test_row_split_env_override(tmp_path):
     assert run("7") == ["7", "7"]
     assert run("0") == ["0", "0"]
     assert run("1") == ["0", "0"]
-    assert run("1000") == ["64", "64"]
+    assert run("1000") == ["32", "32"]
 
 
 def test_row_split_heuristic():
@@ -130,13 +130,13 @@ def test_row_split_heuristic():
         # rows that fit one 32768-score workgroup tile stay whole, whatever the batch
         for B, L in ((64, 32768), (128, 32768), (48, 8192), (1, 2048), (4, 4096), (1024, 8192)):
             assert ets.row_split(B, L, 256) == 0, (B, L)
-        # longer rows are cut into chunks of about 16384 scores, at most 64
+        # longer rows are cut into chunks of about 16384 scores, at most 32
         assert ets.row_split(4, 32769, 256) == 3
         assert ets.row_split(4, 65536, 256) == 4
         assert ets.row_split(2, 100000, 256) == 7
         assert ets.row_split(4, 262144, 256) == 16
         assert ets.row_split(16, 262144, 256) == 16
-        assert ets.row_split(1, 10 ** 7, 256) == 64
+        assert ets.row_split(1, 10 ** 7, 256) == 32
         assert ets.row_split(0, 262144, 256) == 0
         # the grid is held to two workgroups per compute unit ...
         assert ets.row_split(64, 262144, 256) == 8
