@@ -269,3 +269,37 @@ def test_large_row_group_grids():
         w = _raw("large-grid", x, k)
         assert_parity(w, out.cpu().numpy(), run_oracle(w))
         _assert_clean(ws)
+
+
+def _banded(rng, B, L):
+    """Each row: four bands of scores at well-separated centres, each band a
+    few ULPs wide, so that whole bands tie bit for bit."""
+    centres = np.array([-3.0, 0.5, 2.0, 7.0], dtype=np.float32)
+    band = rng.integers(0, 4, size=(B, L))
+    ulps = rng.integers(0, 4, size=(B, L)).astype(np.int32)
+    x = centres[band]
+    return (x.view(np.int32) + ulps).view(np.float32)
+
+
+def _narrow(rng, B, L):
+    """Each row inside [1, 1 + 2^-13): at most 1024 distinct scores."""
+    return (np.float32(1.0).view(np.int32) + rng.integers(0, 1024, size=(B, L)).astype(np.int32)).view(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["banded", "narrow"])
+@pytest.mark.parametrize("g", [0, 4, 16])
+def test_banded_and_narrow_rows(kind, g):
+    """Few distinct scores per row: the threshold falls inside a band of
+    equal keys, resolved by position among equal keys on one workgroup
+    (G = 0) and across a row group."""
+    rng = np.random.default_rng(500 + g)
+    L = 65536
+    x = (_banded if kind == "banded" else _narrow)(rng, 3, L)
+    lens = np.array([L, 40001, 20000], dtype=np.int32)
+    for k in (1, 1024, 2048):
+        print("case", kind, "G", g, "k", k, flush=True)
+        w = _raw(kind, x, k, lens)
+        with split(g):
+            assert_parity(w, run_gpu(w), run_oracle(w))
+    for ws in _cached_workspaces():
+        _assert_clean(ws)
