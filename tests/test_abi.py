@@ -153,3 +153,24 @@ def test_row_split_heuristic():
     finally:
         if env is not None:
             os.environ["ETS_ROW_SPLIT"] = env
+
+
+def test_row_split_bounds_hold_everywhere():
+    """Over a grid of shapes: at most 32 workgroups per row, never a split of a
+    row that fits one 32768-score tile, the grid within two workgroups per
+    compute unit, and never fewer than 3 workgroups in a split."""
+    import exact_top_selection_amd as ets
+    env = os.environ.pop("ETS_ROW_SPLIT", None)
+    try:
+        for cu in (80, 256, 304):
+            for B in (1, 2, 3, 5, 8, 17, 64, 100, 128, 129, 256, 1000):
+                for L in (1, 32768, 32769, 65536, 100000, 262144, 10 ** 6, 2 ** 31 - 1):
+                    g = ets.row_split(B, L, cu)
+                    assert 0 <= g <= 32, (cu, B, L, g)
+                    if L <= 32768:
+                        assert g == 0, (cu, B, L, g)
+                    if g:
+                        assert g >= 3 and B * g <= 2 * cu, (cu, B, L, g)
+    finally:
+        if env is not None:
+            os.environ["ETS_ROW_SPLIT"] = env
