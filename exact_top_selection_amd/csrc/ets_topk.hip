@@ -1224,8 +1224,9 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // Workgroup i is member i % G of row i / G when the whole grid fits the
 // device at once; otherwise groups are formed in the order workgroups start
 // (a ticket counter), so that a workgroup only ever waits for members that
-// have started or start next and progress needs room for one group on the
-// device, not for the whole grid.  Every wait is bounded; on expiry the
+// have started or start next and progress needs room for one group, not
+// for the whole grid: room on one XCD, since near the grid's end only one
+// XCD may still be starting workgroups (hence at most 32 members per row).  Every wait is bounded; on expiry the
 // workspace's error word is set, the call's output is undefined, and the
 // kernel still ends.
 //
@@ -1856,8 +1857,8 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
 // One launch for the whole batch: B * G workgroups, G per row.  TICKET:
 // workgroups take rows in the order they start (a device counter), so that
 // a group only waits for members that have started or start next and
-// progress needs room for one group.  Otherwise workgroup i is member i % G
-// of row i / G; the host chooses this only when the whole grid fits the
+// progress needs room for one group on one XCD (G <= 32).  Otherwise
+// workgroup i is member i % G of row i / G; the host chooses this only when the whole grid fits the
 // device at once (one workgroup per compute unit), where waiting members
 // can never keep the rest of the grid from starting.
 template <int T, int VEC, int MODE, bool V4, bool TICKET>
@@ -1992,8 +1993,12 @@ constexpr int64_t kRowTile = static_cast<int64_t>(kRowThreads) * 4 * kRowVec;
 // row-group path: 1024-lane workgroups, each holding up to VEC float4 per lane
 constexpr int kGroupThreads = 1024;
 constexpr int64_t kGroupChunk = 16384;  // scores per workgroup of a split row
-// 64 members per row tripped the bounded waits (error word set) on grids of
-// 4096 or more workgroups, for a cause not yet found; 32 never did.
+// At most one XCD's compute units: near the end of a ticketed grid the other
+// XCDs may have started all of their share of the workgroups (the dispatcher
+// deals them out by index), and a 1024-lane row-group workgroup fits once per
+// compute unit, so only 32 members of a row are sure to be resident together.
+// 64 members per row ran bounded waits to their limit (error word set) on
+// grids of 4096 or more workgroups; 32 never did.
 constexpr int64_t kMaxGroup = 32;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
