@@ -2007,12 +2007,14 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 // that fits one resident 32768-score tile stays on one workgroup: measured on
 // MI355X, the group's exchanges cost more than the work they spread.  Longer
 // rows are cut into chunks of about kGroupChunk scores, at most kMaxGroup per
-// row, and the whole grid is held to two workgroups per compute unit: a sweep
-// of B in 1..256, row lengths 65536..262144 and 2..64 workgroups per row put
-// the best chunk at 16384 scores while B * G <= 2 * CUs, and one workgroup per
-// row ahead once fewer than four workgroups per row fit that bound (the rows
-// alone then keep every compute unit busy).  cu_count <= 0 (unknown) lifts the
-// bound.  ETS_ROW_SPLIT overrides: 0 or 1 = one workgroup per row, n >= 2 = n
+// row, and the whole grid is held to two workgroups per compute unit unless
+// that would leave a member's chunk larger than one resident tile: a sweep of
+// B in 1..256, row lengths 65536..262144 and 2..64 workgroups per row put the
+// best chunk at 16384 scores while B * G <= 2 * CUs, chunks streamed past one
+// tile well behind resident ones (B = 128, L = 262144: 158 us at G = 4, 99 us
+// at G = 8), and one workgroup per row ahead once B reaches the CU count (the
+// rows alone then keep every compute unit busy).  cu_count <= 0 (unknown)
+// lifts both bounds.  ETS_ROW_SPLIT overrides: 0 or 1 = one workgroup per row, n >= 2 = n
 // workgroups per row (at most kMaxGroup).
 int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count) {
   if (B <= 0 || max_len <= 0) return 0;
@@ -2027,9 +2029,10 @@ int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count) {
   if (max_len <= kRowTile) return 0;
   int64_t G = std::min((max_len + kGroupChunk - 1) / kGroupChunk, kMaxGroup);
   if (cu_count > 0) {
+    if (B >= cu_count) return 0;  // the rows alone keep every compute unit busy
     const int64_t fit = 2 * static_cast<int64_t>(cu_count) / B;  // workgroups per row in 2 * CUs
-    if (fit < 4) return 0;
-    G = std::min(G, fit);
+    const int64_t resident = (max_len + kRowTile - 1) / kRowTile;  // fewest members whose chunks fit one tile
+    G = std::min(G, std::max(fit, resident));
   }
   return static_cast<int32_t>(G);
 }

@@ -142,8 +142,9 @@ ets_status ets_workspace_init(void* workspace, size_t bytes, void* stream);
  * `cu_count` compute units; 0 means one workgroup per row.  Pure host
  * function.  Rows that fit one workgroup's 32768-score tile stay whole;
  * longer rows are cut into chunks of about 16384 scores, at most 32 per row,
- * with B * G held to 2 * cu_count; where that leaves fewer than 4 per row,
- * rows stay whole (cu_count <= 0 lifts that bound).
+ * with B * G held to 2 * cu_count as long as every chunk still fits one
+ * 32768-score tile; from B >= cu_count on, rows stay whole (cu_count <= 0
+ * lifts both bounds).
  * The environment variable ETS_ROW_SPLIT, when set to an integer >= 0,
  * overrides the heuristic (0 or 1: one workgroup per row; n: n workgroups per
  * row, at most 32).  After the pages' row_split heuristic (PR #37591 digest,

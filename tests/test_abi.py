@@ -141,10 +141,12 @@ def test_row_split_heuristic():
         # the grid is held to two workgroups per compute unit ...
         assert ets.row_split(64, 262144, 256) == 8
         assert ets.row_split(64, 65536, 256) == 4
-        assert ets.row_split(128, 262144, 256) == 4
-        assert ets.row_split(64, 10 ** 7, 256) == 8
-        # ... and rows stay whole once fewer than four per row fit it
-        assert ets.row_split(129, 262144, 256) == 0
+        assert ets.row_split(128, 131072, 256) == 4
+        # ... unless that leaves chunks longer than one 32768-score tile ...
+        assert ets.row_split(128, 262144, 256) == 8
+        assert ets.row_split(192, 65536, 256) == 2
+        assert ets.row_split(64, 10 ** 7, 256) == 32
+        # ... and rows stay whole once the batch alone fills the device
         assert ets.row_split(256, 65536, 256) == 0
         assert ets.row_split(4096, 262144, 256) == 0
         # an unknown compute-unit count lifts the bound
@@ -157,8 +159,9 @@ def test_row_split_heuristic():
 
 def test_row_split_bounds_hold_everywhere():
     """Over a grid of shapes: at most 32 workgroups per row, never a split of a
-    row that fits one 32768-score tile, the grid within two workgroups per
-    compute unit, and never fewer than 3 workgroups in a split."""
+    row that fits one 32768-score tile or of a batch that fills the device,
+    and the grid within two workgroups per compute unit unless chunks would
+    outgrow one tile."""
     import exact_top_selection_amd as ets
     env = os.environ.pop("ETS_ROW_SPLIT", None)
     try:
@@ -167,10 +170,11 @@ def test_row_split_bounds_hold_everywhere():
                 for L in (1, 32768, 32769, 65536, 100000, 262144, 10 ** 6, 2 ** 31 - 1):
                     g = ets.row_split(B, L, cu)
                     assert 0 <= g <= 32, (cu, B, L, g)
-                    if L <= 32768:
+                    if L <= 32768 or B >= cu:
                         assert g == 0, (cu, B, L, g)
                     if g:
-                        assert g >= 3 and B * g <= 2 * cu, (cu, B, L, g)
+                        tiles = -(-L // 32768)
+                        assert g >= 2 and B * g <= max(2 * cu, B * tiles), (cu, B, L, g)
     finally:
         if env is not None:
             os.environ["ETS_ROW_SPLIT"] = env
