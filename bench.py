@@ -291,8 +291,8 @@ def main() -> int:
     achieved = abytes / (ms_per_step * 1e-3) / 1e9  # GB/s; one kernel launch per step
 
     # the one kernel a step launches: one workgroup per row, or row groups
-    split = ets.row_split(w.B, w.max_len if w.api == "ragged" else w.L,
-                          torch.cuda.get_device_properties(dev).multi_processor_count)
+    cu, _, cap = ets.device_limits()
+    split = ets.row_split(w.B, w.max_len if w.api == "ragged" else w.L, cu, cap)
     kernel = "group_topk_kernel (%d workgroups per row)" % split if split else "row_topk_kernel"
     result = {
         "metric": METRIC,

@@ -27,9 +27,9 @@ from typing import Optional
 import torch
 
 __all__ = ["topk_raw", "topk_paged", "topk_ragged", "workspace_size", "row_split", "floor_read",
-           "floor_launch",
-           "new_workspace", "workspace_init", "workspace_error", "library_path", "MAX_K",
-           "EtsError"]
+           "floor_launch", "device_limits", "group_cap",
+           "new_workspace", "workspace_init", "workspace_error", "workspace_error_async",
+           "library_path", "MAX_K", "EtsError"]
 
 MAX_K = 2048
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -65,13 +65,18 @@ def _load():
                                            vp, sz, vp]
             lib.ets_topk_ragged.argtypes = [vp, vp, vp, i32, i64, i32, vp, i64, vp, sz, vp]
             lib.ets_workspace_size.argtypes = [i32, i64, i32, i32, ctypes.POINTER(sz)]
-            lib.ets_row_split.argtypes = [i32, i64, i32]
+            lib.ets_row_split.argtypes = [i32, i64, i32, i32]
             lib.ets_workspace_init.argtypes = [vp, sz, vp]
+            lib.ets_workspace_error.argtypes = [vp, sz, vp, vp]
+            pi32 = ctypes.POINTER(i32)
+            lib.ets_device_limits.argtypes = [i32, pi32, pi32, pi32]
+            lib.ets_group_cap.argtypes = [i32, i32, i32]
             lib.ets_status_string.argtypes = [i32]
             lib.ets_floor_read.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp, i64, vp]
             lib.ets_floor_launch.argtypes = [i32, i64, vp]
             for fn in (lib.ets_topk_raw, lib.ets_topk_paged, lib.ets_topk_ragged,
                        lib.ets_workspace_size, lib.ets_row_split, lib.ets_workspace_init,
+                       lib.ets_workspace_error, lib.ets_device_limits, lib.ets_group_cap,
                        lib.ets_floor_read, lib.ets_floor_launch):
                 fn.restype = ctypes.c_int32
             lib.ets_status_string.restype = ctypes.c_char_p
@@ -134,9 +139,24 @@ def workspace_size(B: int, max_row_len: int, k: int, device: Optional[int] = Non
     return nbytes.value
 
 
-def row_split(B: int, max_row_len: int, cu_count: int) -> int:
-    """Blocks per row chosen for (B, max_row_len) on ``cu_count`` CUs (0 = one per row)."""
-    return int(_load().ets_row_split(B, max_row_len, cu_count))
+def row_split(B: int, max_row_len: int, cu_count: int, max_group: int) -> int:
+    """Workgroups per row chosen for (B, max_row_len) on a device with ``cu_count``
+    CUs whose largest row group is ``max_group`` (0 = one per row, -1 = an
+    ETS_ROW_SPLIT override above max_group, which the calls reject)."""
+    return int(_load().ets_row_split(B, max_row_len, cu_count, max_group))
+
+
+def group_cap(cu_count: int, xcd_count: int, groups_per_cu: int) -> int:
+    """Largest row group for a device of these sizes (pure host function)."""
+    return int(_load().ets_group_cap(cu_count, xcd_count, groups_per_cu))
+
+
+def device_limits(device: Optional[int] = None):
+    """(compute units, XCDs, largest row group) of a device (default: current)."""
+    cu, xcd, cap = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(_load().ets_device_limits(-1 if device is None else int(device), ctypes.byref(cu),
+                                     ctypes.byref(xcd), ctypes.byref(cap)), "ets_device_limits")
+    return cu.value, xcd.value, cap.value
 
 
 # Workspace word set non-zero by a call that stopped waiting for the other
@@ -168,9 +188,32 @@ def workspace_init(workspace: torch.Tensor) -> None:
                                           _stream(workspace.device)), "ets_workspace_init")
 
 
-def workspace_error(workspace: torch.Tensor) -> int:
-    """The workspace's error word (synchronises); non-zero means a call timed out."""
-    return int(workspace.view(torch.int32)[WORKSPACE_ERROR_WORD].item())
+def workspace_error_async(workspace: Optional[torch.Tensor], flag: torch.Tensor) -> None:
+    """Enqueues a copy of the workspace's error word into ``flag`` (int32 [>=1] on
+    the same device) and clears the word, on the current stream, without
+    synchronising.  ``workspace`` None (a call that needed none) writes 0."""
+    _require(flag, "flag", torch.int32, 1)
+    if flag.numel() < 1:
+        raise ValueError("flag needs one element")
+    dev = flag.device
+    if workspace is not None:
+        _require(workspace, "workspace", torch.uint8, 1)
+        if workspace.device != dev:
+            raise ValueError("flag must be on the workspace's device")
+    with torch.cuda.device(dev):
+        _check(_load().ets_workspace_error(
+            workspace.data_ptr() if workspace is not None else None,
+            workspace.numel() if workspace is not None else 0, flag.data_ptr(), _stream(dev)),
+            "ets_workspace_error")
+
+
+def workspace_error(workspace: Optional[torch.Tensor]) -> int:
+    """The workspace's error word, cleared afterwards (synchronises).  Non-zero
+    means a call stopped waiting for its row group and its output is undefined."""
+    dev = workspace.device if workspace is not None else torch.device("cuda", torch.cuda.current_device())
+    flag = torch.full((1,), -1, dtype=torch.int32, device=dev)
+    workspace_error_async(workspace, flag)
+    return int(flag.item())
 
 
 def _workspace(B: int, max_len: int, k: int, device: torch.device,
@@ -180,6 +223,12 @@ def _workspace(B: int, max_len: int, k: int, device: torch.device,
     if need == 0:
         return None, 0
     if workspace is None:
+        if torch.cuda.is_current_stream_capturing():
+            # a captured graph keeps the buffer's address for its replays, and
+            # the shared buffer may be replaced by a larger one later
+            raise ValueError("a call that needs a workspace (%d bytes) must be given one "
+                             "while a graph is being captured: pass workspace=new_workspace(...)"
+                             % need)
         key = (device.index, _stream(device))
         with _lock:
             workspace = _ws_cache.get(key)
@@ -322,8 +371,9 @@ def floor_read(scores: torch.Tensor, lens: Optional[torch.Tensor] = None,
         if max_len is None:
             raise ValueError("ragged rows need max_len")
         L, stride = 0, 0
-    cu = torch.cuda.get_device_properties(dev).multi_processor_count
-    words = B * max(1, row_split(B, max_len, cu))
+    with torch.cuda.device(dev):
+        cu, _, cap = device_limits()
+    words = B * max(1, row_split(B, max_len, cu, cap))
     if sink is None:
         sink = torch.empty(max(words, 1), dtype=torch.int32, device=dev)
     _require(sink, "sink", torch.int32, 1)

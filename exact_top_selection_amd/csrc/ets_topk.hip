@@ -776,7 +776,7 @@ __device__ __forceinline__ Sel early_round(const SpanT& span, uint32_t (&key)[4 
     hi = max(hi, red[w]);
     lb = min(lb, red[16 + w]);
   }
-  const int32_t nfull = min(LB, max(0, (n - jth) / 4 + 1));
+  const int32_t nfull = n >= jth ? min(LB, (n - jth) / 4 + 1) : 0;
   uint32_t lo = nfull * jth >= k ? lb : 0u;
   auto shift_of = [](uint32_t span) {
     int sh = span ? 32 - __clz(static_cast<int>(span)) : 0;
@@ -974,7 +974,7 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kS
   // scalar: t and t + T)
   const int32_t jpos = V4 ? 4 * tid + jth - 1 : (jth - 1) * T + tid;
   const bool full = jth <= 2 && jpos < n;
-  const int32_t nfull = jth > 2 ? 0 : (V4 ? min(T, max(0, (n - jth) / 4 + 1)) : min(T, max(0, n - (jth - 1) * T)));
+  const int32_t nfull = jth > 2 ? 0 : (V4 ? (n >= jth ? min(T, (n - jth) / 4 + 1) : 0) : min(T, max(0, n - (jth - 1) * T)));
   Sel sel0{};
   {
     const uint32_t rmax = wave_reduce(m1, OpMax());
@@ -1222,20 +1222,40 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 //    and returns the row's workspace to zero.
 //
 // Workgroup i is member i % G of row i / G when the whole grid fits the
-// device at once; otherwise groups are formed in the order workgroups start
-// (a ticket counter), so that a workgroup only ever waits for members that
-// have started or start next and progress needs room for one group, not
-// for the whole grid: room on one XCD, since near the grid's end only one
-// XCD may still be starting workgroups (hence at most 32 members per row).  Every wait is bounded; on expiry the
-// workspace's error word is set, the call's output is undefined, and the
-// kernel still ends.
-//
-// Data crosses workgroups only through device-scope relaxed atomics (loads
-// and stores are issued coherent at device scope, read-modify-writes are
-// performed in the memory hierarchy), with each wave's memory counter drained
-// before an arrival is counted (or, for the coarse table, completion read
-// from the table's own total), so no cache write-back or invalidate is
-// needed.
+// device's row-group slots at once; otherwise groups are formed in the order
+// workgroups start (a ticket counter).  Why a ticketed grid always finishes
+// when G is at most the row-group slots of one XCD (its compute units times
+// the workgroups one compute unit holds; the host derives that cap from the
+// device): tickets are consecutive, so every group whose G tickets are all
+// taken has all of its members started, waits only for them and finishes;
+// only the group holding the newest ticket can be incomplete, with at most
+// G - 1 started members waiting.  The dispatcher deals workgroups to XCDs by
+// index, so near the end of the grid only one XCD may still be starting
+// them; the waiting members occupy at most G - 1 of its slots, so a slot
+// frees up as the complete groups finish, the next workgroup starts and takes
+// the next ticket.  With G above one XCD's slots the incomplete group can
+// hold every slot of the last XCD while its missing members are queued
+// behind them there: a wait then runs to its bound.  Every wait is bounded;
+// on expiry the workspace's error word is set, the call's output is
+// undefined, and the kernel still ends.
+
+// Data crosses workgroups only through agent-scope relaxed atomics, with each
+// wave's memory counter drained before an arrival is counted (or, for the
+// coarse table, completion read from the table's own total).  Why this is
+// enough on gfx942/gfx950 (LLVM AMDGPU usage guide, "Memory Model GFX942",
+// which gfx950 follows): an agent-scope atomic load, store or
+// read-modify-write is issued with the sc1 bit, so it is performed at the
+// device's point of coherence rather than in one XCD's L2 or a compute
+// unit's L1, and two workgroups on different XCDs see one value per
+// location.  What an agent-scope release adds on top of that is a write-back
+// of the L2 (for ordinary stores) and the s_waitcnt vmcnt(0) that waits for
+// the completion of every earlier memory access; the acquire side adds an L1
+// and L2 invalidate (for ordinary loads).  Here every word that one
+// workgroup writes and another reads (slots, tables, counters, cursor, tie
+// list) is written and read by such atomics, so no ordinary access needs the
+// write-back or the invalidate, and the completion wait is drain_vmem()
+// before the arrival that publishes the data.  The output rows are written
+// with ordinary stores but never read inside the kernel.
 //
 // Workspace (u32 words): hdr[64], then per row rec[192] (counters, then one
 // u64 slot per member) | hist[3][4096] | ties[kTieCap] (u64).  It must be
@@ -1528,7 +1548,9 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     const int32_t jth = holders > 0 ? (k + holders - 1) / holders : 3;
     const int32_t jpos = V4 ? 4 * tid + jth - 1 : (jth - 1) * T + tid;
     const bool full = jth <= 2 && span.start + jpos < span.end;
-    const int32_t nfull = jth > 2 ? 0 : (V4 ? min(T, max(0, (nc - jth) / 4 + 1)) : min(T, max(0, nc - (jth - 1) * T)));
+    // lanes whose first jth slots hold scores: float4 lane t holds positions
+    // 4t .. 4t + 3 of the chunk, so 4t + jth - 1 < nc; none when nc < jth
+    const int32_t nfull = jth > 2 ? 0 : (V4 ? (nc >= jth ? min(T, (nc - jth) / 4 + 1) : 0) : min(T, max(0, nc - (jth - 1) * T)));
     const uint32_t vmax = wave_reduce(m1, OpMax());
     const uint32_t vlb = wave_reduce(full ? (jth == 1 ? m1 : m2) : 0xFFFFFFFFu, OpMin());
     if (__lane_id() == 0) {
@@ -1857,10 +1879,12 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
 // One launch for the whole batch: B * G workgroups, G per row.  TICKET:
 // workgroups take rows in the order they start (a device counter), so that
 // a group only waits for members that have started or start next and
-// progress needs room for one group on one XCD (G <= 32).  Otherwise
-// workgroup i is member i % G of row i / G; the host chooses this only when the whole grid fits the
-// device at once (one workgroup per compute unit), where waiting members
-// can never keep the rest of the grid from starting.
+// progress needs room for one group on one XCD (G at most one XCD's
+// row-group slots, checked by the host).  Otherwise workgroup i is member
+// i % G of row i / G; the host chooses this only when the whole grid fits
+// the device's row-group slots at once, where waiting members can never keep
+// the rest of the grid from starting (work of other streams that holds
+// compute units only delays them, until it ends).
 template <int T, int VEC, int MODE, bool V4, bool TICKET>
 __global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, int32_t B, int32_t G) {
   __shared__ GroupSmem sm;
@@ -1873,7 +1897,11 @@ __global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, i
   }
   const int b = static_cast<int>(ticket / static_cast<uint32_t>(G));
   const int g = static_cast<int>(ticket % static_cast<uint32_t>(G));
-  if (b < B) {  // always, unless the workspace was not zero
+  if (b >= B) {
+    // only a workspace that was not zero (a stale ticket) gets here: this
+    // workgroup's chunk goes unselected, so the call's output is undefined
+    if (threadIdx.x == 0) st_dev(w.hdr + kHdrError, 2u);
+  } else {
     const RowRef<MODE> r(p, b);
     if (r.n <= p.k) {
       if (g == 0) emit_whole_row<T, MODE>(p, r);
@@ -1904,6 +1932,18 @@ __global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, i
 // Zero-fills a workspace (words of 4 bytes).
 __global__ __launch_bounds__(256) void workspace_clear(uint32_t* ws, int64_t words) {
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < words; i += 256ll * gridDim.x) ws[i] = 0u;
+}
+
+// Copies a workspace's error word to flag[0] and clears it (ws may be null:
+// flag[0] = 0).  One lane; ordered after earlier work on the same stream.
+__global__ __launch_bounds__(64) void workspace_error_take(uint32_t* ws, int32_t* flag) {
+  if (threadIdx.x != 0) return;
+  uint32_t e = 0;
+  if (ws != nullptr) {
+    e = ld_dev(ws + kHdrError);
+    st_dev(ws + kHdrError, 0u);
+  }
+  flag[0] = static_cast<int32_t>(e);
 }
 
 // ---------------------------------------------------------------- measurement floors
@@ -1950,11 +1990,29 @@ struct DeviceInfo {
   bool queried = false;
   bool supported = false;
   int cu_count = 0;
+  int xcd_count = 0;   // XCDs (dies with their own L2 and workgroup dispatcher)
+  int group_occ = 0;   // row-group workgroups one compute unit holds at once
+  int group_cap = 0;   // largest row group whose members fit the slots of one XCD
 };
 
 constexpr int kMaxDevices = 64;
 std::mutex g_dev_mutex;
 DeviceInfo g_dev[kMaxDevices];
+
+int group_kernel_occupancy();  // fewest resident workgroups per CU over the row-group kernels
+
+// Slots in a row's workspace record: the most members a row group can have.
+constexpr int kGroupSlotCap = 64;
+
+// The largest row group that is sure to make progress: a group waits only for
+// its own members, and near the end of a ticketed grid only one XCD may still
+// be starting workgroups, so a group of G must fit the row-group slots of one
+// XCD (its compute units times the workgroups one compute unit holds).
+int32_t group_cap_of(int32_t cu_count, int32_t xcd_count, int32_t per_cu) {
+  if (cu_count <= 0 || xcd_count <= 0 || per_cu <= 0) return 0;
+  const int64_t slots = static_cast<int64_t>(cu_count / xcd_count) * per_cu;
+  return static_cast<int32_t>(std::min<int64_t>(slots, kGroupSlotCap));
+}
 
 ets_status device_info(int dev, DeviceInfo* info_out) {
   if (dev < 0 || dev >= kMaxDevices) return ETS_ERR_DEVICE;
@@ -1965,6 +2023,20 @@ ets_status device_info(int dev, DeviceInfo* info_out) {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ETS_ERR_DEVICE;
     d.supported = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     d.cu_count = prop.multiProcessorCount;
+    int xcc = 0;
+    if (hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcc <= 0)
+      return ETS_ERR_DEVICE;
+    d.xcd_count = xcc;
+    if (d.supported) {
+      // occupancy queries refer to the current device
+      int cur = -1;
+      if (hipGetDevice(&cur) != hipSuccess) return ETS_ERR_DEVICE;
+      if (cur != dev && hipSetDevice(dev) != hipSuccess) return ETS_ERR_DEVICE;
+      d.group_occ = group_kernel_occupancy();
+      if (cur != dev) (void)hipSetDevice(cur);
+      if (d.group_occ <= 0) return ETS_ERR_DEVICE;
+      d.group_cap = group_cap_of(d.cu_count, d.xcd_count, d.group_occ);
+    }
     d.queried = true;
   }
   if (!d.supported) return ETS_ERR_DEVICE;
@@ -1993,43 +2065,70 @@ constexpr int64_t kRowTile = static_cast<int64_t>(kRowThreads) * 4 * kRowVec;
 // row-group path: 1024-lane workgroups, each holding up to VEC float4 per lane
 constexpr int kGroupThreads = 1024;
 constexpr int64_t kGroupChunk = 16384;  // scores per workgroup of a split row
-// At most one XCD's compute units: near the end of a ticketed grid the other
-// XCDs may have started all of their share of the workgroups (the dispatcher
-// deals them out by index), and a 1024-lane row-group workgroup fits once per
-// compute unit, so only 32 members of a row are sure to be resident together.
-// 64 members per row ran bounded waits to their limit (error word set) on
-// grids of 4096 or more workgroups; 32 never did.
-constexpr int64_t kMaxGroup = 32;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-// Workgroups per row (0 = one workgroup per row on the row kernel).  A row
+template <int MODE, bool V4, int VEC, bool TICKET>
+int occupancy_of() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&ets::group_topk_kernel<kGroupThreads, VEC, MODE, V4, TICKET>),
+          kGroupThreads, 0) != hipSuccess)
+    return 0;
+  return n;
+}
+template <int MODE, bool V4, bool TICKET>
+int occupancy_vecs() {
+  return std::min(std::min(occupancy_of<MODE, V4, 1, TICKET>(), occupancy_of<MODE, V4, 2, TICKET>()),
+                  std::min(occupancy_of<MODE, V4, 4, TICKET>(), occupancy_of<MODE, V4, 8, TICKET>()));
+}
+int group_kernel_occupancy() {
+  int m = occupancy_vecs<ets::kRagged, false, false>();
+  m = std::min(m, occupancy_vecs<ets::kRagged, false, true>());
+  m = std::min(m, occupancy_vecs<ets::kRaw, false, false>());
+  m = std::min(m, occupancy_vecs<ets::kRaw, false, true>());
+  m = std::min(m, occupancy_vecs<ets::kRaw, true, false>());
+  m = std::min(m, occupancy_vecs<ets::kRaw, true, true>());
+  m = std::min(m, occupancy_vecs<ets::kPaged, false, false>());
+  m = std::min(m, occupancy_vecs<ets::kPaged, false, true>());
+  m = std::min(m, occupancy_vecs<ets::kPaged, true, false>());
+  m = std::min(m, occupancy_vecs<ets::kPaged, true, true>());
+  return m;
+}
+
+// Workgroups per row (0 = one workgroup per row on the row kernel; -1 = an
+// ETS_ROW_SPLIT override above max_group, which the calls reject).  A row
 // that fits one resident 32768-score tile stays on one workgroup: measured on
 // MI355X, the group's exchanges cost more than the work they spread.  Longer
-// rows are cut into chunks of about kGroupChunk scores, at most kMaxGroup per
+// rows are cut into chunks of about kGroupChunk scores, at most max_group per
 // row, and the whole grid is held to two workgroups per compute unit unless
 // that would leave a member's chunk larger than one resident tile: a sweep of
 // B in 1..256, row lengths 65536..262144 and 2..64 workgroups per row put the
 // best chunk at 16384 scores while B * G <= 2 * CUs, chunks streamed past one
 // tile well behind resident ones (B = 128, L = 262144: 158 us at G = 4, 99 us
 // at G = 8), and one workgroup per row ahead once B reaches the CU count (the
-// rows alone then keep every compute unit busy).  cu_count <= 0 (unknown)
-// lifts both bounds.  ETS_ROW_SPLIT overrides: 0 or 1 = one workgroup per row, n >= 2 = n
-// workgroups per row (at most kMaxGroup).
-int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count) {
+// rows alone then keep every compute unit busy) and where more than half the
+// compute units hold a row of at most two tiles (B = 192, L = 65536: 45.7 us
+// one per row, 48.7 at G = 2).  cu_count <= 0 (unknown) lifts the grid
+// bounds; max_group <= 0 (unknown) leaves the workspace's slot count as the
+// only cap.  ETS_ROW_SPLIT overrides: 0 or 1 = one workgroup per row, n >= 2
+// = n workgroups per row, n <= max_group.
+int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count, int32_t max_group) {
   if (B <= 0 || max_len <= 0) return 0;
+  const int64_t cap = max_group > 0 ? std::min<int64_t>(max_group, kGroupSlotCap) : kGroupSlotCap;
   if (const char* e = std::getenv("ETS_ROW_SPLIT"); e != nullptr && *e != '\0') {
     char* end = nullptr;
     const long v = std::strtol(e, &end, 10);
     if (end != e && *end == '\0' && v >= 0) {
       if (v <= 1) return 0;
-      return static_cast<int32_t>(std::min<int64_t>(v, kMaxGroup));
+      return v <= cap ? static_cast<int32_t>(v) : -1;
     }
   }
   if (max_len <= kRowTile) return 0;
-  int64_t G = std::min((max_len + kGroupChunk - 1) / kGroupChunk, kMaxGroup);
+  int64_t G = std::min((max_len + kGroupChunk - 1) / kGroupChunk, cap);
   if (cu_count > 0) {
     if (B >= cu_count) return 0;  // the rows alone keep every compute unit busy
+    if (max_len <= 2 * kRowTile && 2 * static_cast<int64_t>(B) > cu_count) return 0;
     const int64_t fit = 2 * static_cast<int64_t>(cu_count) / B;  // workgroups per row in 2 * CUs
     const int64_t resident = (max_len + kRowTile - 1) / kRowTile;  // fewest members whose chunks fit one tile
     G = std::min(G, std::max(fit, resident));
@@ -2042,10 +2141,12 @@ size_t group_ws_bytes(int32_t B) {
   return (ets::kHdrWords + static_cast<size_t>(B) * per_row) * 4;
 }
 
-// Host-side check of the row-group path's workspace, before anything is enqueued.
-ets_status check_workspace(int32_t B, int64_t max_len, int32_t cu_count, const void* ws,
+// Host-side check of a call's launch plan and of the row-group path's
+// workspace, before anything is enqueued.
+ets_status check_workspace(int32_t B, int64_t max_len, const DeviceInfo& info, const void* ws,
                            size_t ws_bytes) {
-  const int32_t G = split_plan(B, max_len, cu_count);
+  const int32_t G = split_plan(B, max_len, info.cu_count, info.group_cap);
+  if (G < 0) return ETS_ERR_INVALID_ARG;
   if (G == 0) return ETS_OK;
   if (static_cast<int64_t>(B) * G > INT32_MAX) return ETS_ERR_INVALID_ARG;
   if (!ws || ws_bytes < group_ws_bytes(B) || !aligned16(ws)) return ETS_ERR_WORKSPACE;
@@ -2058,11 +2159,15 @@ void launch_rows(const ets::Params& p, int32_t B, hipStream_t stream) {
                      p);
 }
 
+// Members are assigned by workgroup index only when the whole grid fits the
+// device's row-group slots at once (each compute unit holds group_occ of
+// them); otherwise by ticket in start order (see group_topk_kernel).
 template <int MODE, bool V4, int VEC>
-void launch_group(const ets::Params& p, int32_t B, int32_t G, int32_t cu_count, void* ws,
+void launch_group(const ets::Params& p, int32_t B, int32_t G, const DeviceInfo& info, void* ws,
                   hipStream_t stream) {
   const uint32_t grid = static_cast<uint32_t>(B) * static_cast<uint32_t>(G);
-  if (grid <= static_cast<uint32_t>(cu_count)) {
+  const int64_t slots = static_cast<int64_t>(info.cu_count) * info.group_occ;
+  if (static_cast<int64_t>(grid) <= slots) {
     hipLaunchKernelGGL((ets::group_topk_kernel<kGroupThreads, VEC, MODE, V4, false>), dim3(grid),
                        dim3(kGroupThreads), 0, stream, p, static_cast<uint32_t*>(ws), B, G);
   } else {
@@ -2082,9 +2187,9 @@ struct Shape {
   bool stream;
 };
 
-Shape launch_shape(int32_t B, int64_t max_len, int32_t cu_count) {
-  const int32_t G = split_plan(B, max_len, cu_count);
-  if (G == 0) {
+Shape launch_shape(int32_t B, int64_t max_len, const DeviceInfo& info) {
+  const int32_t G = split_plan(B, max_len, info.cu_count, info.group_cap);
+  if (G <= 0) {
     if (max_len <= 2048) return {1, 512, 1, false};
     if (max_len <= 4096) return {1, kRowThreads, 1, false};
     if (max_len <= kRowTile / 4) return {1, kRowThreads, kRowVec / 4, false};
@@ -2098,9 +2203,9 @@ Shape launch_shape(int32_t B, int64_t max_len, int32_t cu_count) {
 }
 
 template <int MODE, bool V4>
-ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, int32_t cu_count, void* ws,
+ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, const DeviceInfo& info, void* ws,
                   hipStream_t stream) {
-  const Shape sh = launch_shape(B, max_len, cu_count);
+  const Shape sh = launch_shape(B, max_len, info);
   if (sh.groups == 1) {
     if (sh.threads == 512) {
       launch_rows<MODE, V4, 512, 1, false>(p, B, stream);
@@ -2119,13 +2224,13 @@ ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, int32_t cu_c
   }
   // (workspace already validated by check_workspace)
   if (sh.vec == 1) {
-    launch_group<MODE, V4, 1>(p, B, sh.groups, cu_count, ws, stream);
+    launch_group<MODE, V4, 1>(p, B, sh.groups, info, ws, stream);
   } else if (sh.vec == 2) {
-    launch_group<MODE, V4, 2>(p, B, sh.groups, cu_count, ws, stream);
+    launch_group<MODE, V4, 2>(p, B, sh.groups, info, ws, stream);
   } else if (sh.vec == 4) {
-    launch_group<MODE, V4, 4>(p, B, sh.groups, cu_count, ws, stream);
+    launch_group<MODE, V4, 4>(p, B, sh.groups, info, ws, stream);
   } else {
-    launch_group<MODE, V4, 8>(p, B, sh.groups, cu_count, ws, stream);
+    launch_group<MODE, V4, 8>(p, B, sh.groups, info, ws, stream);
   }
   return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
 }
@@ -2166,7 +2271,8 @@ ets_status ets_floor_read(const float* scores, int64_t row_stride, int32_t B, in
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
   const int64_t max_len = ragged ? max_len_hint : L;
-  const Shape sh = launch_shape(B, max_len, info.cu_count);
+  if (split_plan(B, max_len, info.cu_count, info.group_cap) < 0) return ETS_ERR_INVALID_ARG;
+  const Shape sh = launch_shape(B, max_len, info);
   const int64_t grid = static_cast<int64_t>(B) * sh.groups;
   if (grid > INT32_MAX || sink_words < grid) return ETS_ERR_INVALID_ARG;
   ets::Params p{};
@@ -2193,7 +2299,8 @@ ets_status ets_floor_launch(int32_t B, int64_t max_row_len, void* stream) {
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
-  const Shape sh = launch_shape(B, max_row_len, info.cu_count);
+  if (split_plan(B, max_row_len, info.cu_count, info.group_cap) < 0) return ETS_ERR_INVALID_ARG;
+  const Shape sh = launch_shape(B, max_row_len, info);
   const int64_t grid = static_cast<int64_t>(B) * sh.groups;
   if (grid > INT32_MAX) return ETS_ERR_INVALID_ARG;
   auto s = static_cast<hipStream_t>(stream);
@@ -2217,8 +2324,8 @@ const char* ets_status_string(ets_status status) {
   }
 }
 
-int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count) {
-  return split_plan(B, max_row_len, cu_count);
+int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count, int32_t max_group) {
+  return split_plan(B, max_row_len, cu_count, max_group);
 }
 
 ets_status ets_workspace_size(int32_t B, int64_t max_row_len, int32_t k, int32_t device,
@@ -2229,7 +2336,8 @@ ets_status ets_workspace_size(int32_t B, int64_t max_row_len, int32_t k, int32_t
   int dev = device;
   if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return ETS_ERR_DEVICE;
   if (ets_status st = device_info(dev, &info); st != ETS_OK) return st;
-  const int32_t G = split_plan(B, max_row_len, info.cu_count);
+  const int32_t G = split_plan(B, max_row_len, info.cu_count, info.group_cap);
+  if (G < 0) return ETS_ERR_INVALID_ARG;
   *bytes = (G == 0 || B == 0) ? 0 : group_ws_bytes(B);
   return ETS_OK;
 }
@@ -2244,6 +2352,33 @@ ets_status ets_workspace_init(void* workspace, size_t workspace_bytes, void* str
   return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
 }
 
+ets_status ets_workspace_error(void* workspace, size_t workspace_bytes, int32_t* flag, void* stream) {
+  if (!flag) return ETS_ERR_INVALID_ARG;
+  if (workspace_bytes != 0 && (!workspace || !aligned16(workspace) ||
+                               workspace_bytes < static_cast<size_t>(ets::kHdrWords) * 4))
+    return ETS_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(ets::workspace_error_take, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     workspace_bytes != 0 ? static_cast<uint32_t*>(workspace) : nullptr, flag);
+  return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
+}
+
+ets_status ets_device_limits(int32_t device, int32_t* cu_count, int32_t* xcd_count,
+                             int32_t* group_cap) {
+  if (!cu_count || !xcd_count || !group_cap) return ETS_ERR_INVALID_ARG;
+  int dev = device;
+  if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return ETS_ERR_DEVICE;
+  DeviceInfo info;
+  if (ets_status st = device_info(dev, &info); st != ETS_OK) return st;
+  *cu_count = info.cu_count;
+  *xcd_count = info.xcd_count;
+  *group_cap = info.group_cap;
+  return ETS_OK;
+}
+
+int32_t ets_group_cap(int32_t cu_count, int32_t xcd_count, int32_t groups_per_cu) {
+  return group_cap_of(cu_count, xcd_count, groups_per_cu);
+}
+
 ets_status ets_topk_raw(const float* scores, int64_t row_stride, int32_t B, int32_t L,
                         const int32_t* lens, int32_t k, int32_t* out, int64_t out_stride,
                         void* workspace, size_t workspace_bytes, void* stream) {
@@ -2254,7 +2389,7 @@ ets_status ets_topk_raw(const float* scores, int64_t row_stride, int32_t B, int3
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
-  if (ets_status st = check_workspace(B, L, info.cu_count, workspace, workspace_bytes); st != ETS_OK)
+  if (ets_status st = check_workspace(B, L, info, workspace, workspace_bytes); st != ETS_OK)
     return st;
   ets::Params p{};
   p.scores = scores;
@@ -2267,8 +2402,8 @@ ets_status ets_topk_raw(const float* scores, int64_t row_stride, int32_t B, int3
   p.page_shift = -1;
   const bool v4 = aligned16(scores) && (row_stride % 4 == 0) && (L % 4 == 0);
   auto s = static_cast<hipStream_t>(stream);
-  return v4 ? launch<ets::kRaw, true>(p, B, L, info.cu_count, workspace, s)
-            : launch<ets::kRaw, false>(p, B, L, info.cu_count, workspace, s);
+  return v4 ? launch<ets::kRaw, true>(p, B, L, info, workspace, s)
+            : launch<ets::kRaw, false>(p, B, L, info, workspace, s);
 }
 
 ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, int32_t L,
@@ -2283,7 +2418,7 @@ ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, in
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
-  if (ets_status st = check_workspace(B, L, info.cu_count, workspace, workspace_bytes); st != ETS_OK)
+  if (ets_status st = check_workspace(B, L, info, workspace, workspace_bytes); st != ETS_OK)
     return st;
   ets::Params p{};
   p.scores = scores;
@@ -2299,8 +2434,8 @@ ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, in
   p.out_stride = out_stride;
   const bool v4 = aligned16(scores) && (row_stride % 4 == 0) && (L % 4 == 0);
   auto s = static_cast<hipStream_t>(stream);
-  return v4 ? launch<ets::kPaged, true>(p, B, L, info.cu_count, workspace, s)
-            : launch<ets::kPaged, false>(p, B, L, info.cu_count, workspace, s);
+  return v4 ? launch<ets::kPaged, true>(p, B, L, info, workspace, s)
+            : launch<ets::kPaged, false>(p, B, L, info, workspace, s);
 }
 
 ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,
@@ -2314,7 +2449,7 @@ ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
-  if (ets_status st = check_workspace(B, max_len_hint, info.cu_count, workspace, workspace_bytes);
+  if (ets_status st = check_workspace(B, max_len_hint, info, workspace, workspace_bytes);
       st != ETS_OK)
     return st;
   ets::Params p{};
@@ -2325,7 +2460,7 @@ ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,
   p.out = out;
   p.out_stride = out_stride;
   p.page_shift = -1;
-  return launch<ets::kRagged, false>(p, B, max_len_hint, info.cu_count, workspace,
+  return launch<ets::kRagged, false>(p, B, max_len_hint, info, workspace,
                                      static_cast<hipStream_t>(stream));
 }
 

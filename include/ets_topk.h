@@ -45,10 +45,15 @@
  *     and every call returns the counters and tables it relies on to zero
  *     (other words may keep stale data), so one workspace serves any number
  *     of calls, including replays of a captured graph.  It must not be
- *     shared by calls that may run concurrently.  The 32-bit word at byte
- *     offset 128 is set non-zero if a call stopped waiting for the other
- *     workgroups of a row (only possible when other work keeps the device
- *     full for a very long time); that call's output is then undefined.
+ *     shared by calls that may run concurrently.
+ *   - A split row's workgroups wait for one another on the device, and every
+ *     such wait is bounded.  A wait runs out only when other work keeps the
+ *     device's compute units for a very long time, or when the workspace was
+ *     not zero (a stale ticket); the call has already returned ETS_OK by then,
+ *     so the kernel records the failure in the workspace's error word (the
+ *     32-bit word at byte offset 128) and that call's output is undefined.
+ *     ets_workspace_error() copies and clears that word on the stream without
+ *     synchronising; check it after the calls whose results matter.
  */
 #ifndef ETS_TOPK_H
 #define ETS_TOPK_H
@@ -138,19 +143,50 @@ ets_status ets_workspace_size(int32_t B, int64_t max_row_len, int32_t k, int32_t
 ets_status ets_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /*
+ * Enqueues on `stream` a copy of the workspace's error word into flag[0]
+ * (device int32, caller-owned) and clears the word, so that the next calls
+ * start clean.  Non-zero means a call before it on the stream stopped waiting
+ * for the other workgroups of a row (1: a bounded wait ran out; 2: a stale
+ * ticket in a workspace that was not zero) and its output is undefined.
+ * workspace_bytes = 0 (a call that needed no workspace) writes 0; otherwise
+ * workspace must be 16-byte aligned and at least 256 bytes.  Nothing is
+ * synchronised: read flag after the stream reaches it.
+ */
+ets_status ets_workspace_error(void* workspace, size_t workspace_bytes, int32_t* flag, void* stream);
+
+/*
+ * The device's compute units, XCDs and the largest row group the library
+ * forms on it (device = -1: the current device): one XCD's compute units
+ * times the row-group workgroups one compute unit holds (from the HIP
+ * occupancy query of the row-group kernels), at most 64.  A group of G
+ * workgroups waits only for its own members, so it must fit the slots of the
+ * one XCD that may still be starting workgroups near a grid's end.
+ */
+ets_status ets_device_limits(int32_t device, int32_t* cu_count, int32_t* xcd_count,
+                             int32_t* group_cap);
+
+/* The cap of ets_device_limits from its inputs (pure host function; 0 if any
+ * input is <= 0): min(64, (cu_count / xcd_count) * groups_per_cu). */
+int32_t ets_group_cap(int32_t cu_count, int32_t xcd_count, int32_t groups_per_cu);
+
+/*
  * Workgroups per row the library uses for (B, max_row_len) on a device with
- * `cu_count` compute units; 0 means one workgroup per row.  Pure host
- * function.  Rows that fit one workgroup's 32768-score tile stay whole;
- * longer rows are cut into chunks of about 16384 scores, at most 32 per row,
- * with B * G held to 2 * cu_count as long as every chunk still fits one
- * 32768-score tile; from B >= cu_count on, rows stay whole (cu_count <= 0
- * lifts both bounds).
+ * `cu_count` compute units whose largest row group is `max_group`
+ * (ets_device_limits); 0 means one workgroup per row.  Pure host function.
+ * Rows that fit one workgroup's 32768-score tile stay whole; longer rows are
+ * cut into chunks of about 16384 scores, at most max_group per row, with
+ * B * G held to 2 * cu_count as long as every chunk still fits one
+ * 32768-score tile; from B >= cu_count on, and for rows of at most 65536
+ * scores once B > cu_count / 2, rows stay whole (cu_count <= 0 lifts these
+ * bounds; max_group <= 0 caps G at 64, the workspace's member slots).
  * The environment variable ETS_ROW_SPLIT, when set to an integer >= 0,
  * overrides the heuristic (0 or 1: one workgroup per row; n: n workgroups per
- * row, at most 32).  After the pages' row_split heuristic (PR #37591 digest,
- * the topk.hip excerpt), with constants of this library measured on MI355X.
+ * row).  An override above max_group returns -1, and the selection calls,
+ * ets_workspace_size and the floors then return ETS_ERR_INVALID_ARG.  After
+ * the pages' row_split heuristic (PR #37591 digest, the topk.hip excerpt),
+ * with constants of this library measured on MI355X.
  */
-int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count);
+int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count, int32_t max_group);
 
 /*
  * Measurement floors.  Neither selects anything: they give the cost of the

@@ -28,7 +28,8 @@ def lib():
 
 def test_header_declares_the_api():
     assert {"ets_topk_raw", "ets_topk_paged", "ets_topk_ragged", "ets_workspace_size",
-            "ets_workspace_init", "ets_row_split", "ets_status_string"} <= set(_declared())
+            "ets_workspace_init", "ets_workspace_error", "ets_device_limits", "ets_group_cap",
+            "ets_row_split", "ets_status_string"} <= set(_declared())
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -108,19 +109,50 @@ def test_workspace_init_validation(lib):
     assert lib.ets_workspace_init(ctypes.c_void_p(0x1004), 256, None) == 1
 
 
+def test_workspace_error_validation(lib):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    # a flag buffer is required; a workspace must be aligned and hold the header
+    assert lib.ets_workspace_error(fake, 4096, None, None) == 1
+    assert lib.ets_workspace_error(None, 4096, fake, None) == 1
+    assert lib.ets_workspace_error(ctypes.c_void_p(0x1004), 4096, fake, None) == 1
+    assert lib.ets_workspace_error(fake, 128, fake, None) == 1
+
+
+def test_device_limits_validation(lib):
+    x = ctypes.c_int32(0)
+    assert lib.ets_device_limits(-1, None, ctypes.byref(x), ctypes.byref(x)) == 1
+    assert lib.ets_device_limits(-1, ctypes.byref(x), None, ctypes.byref(x)) == 1
+
+
+def test_group_cap():
+    """One XCD's compute units times the row-group workgroups each holds, at
+    most the 64 member slots of a row's workspace record."""
+    import exact_top_selection_amd as ets
+    assert ets.group_cap(256, 8, 1) == 32   # MI355X: 32 CUs per XCD, one 1024-lane workgroup each
+    assert ets.group_cap(256, 8, 2) == 64
+    assert ets.group_cap(304, 8, 1) == 38
+    assert ets.group_cap(304, 8, 3) == 64
+    assert ets.group_cap(80, 1, 1) == 64
+    assert ets.group_cap(0, 8, 1) == 0 and ets.group_cap(256, 0, 1) == 0 and ets.group_cap(256, 8, 0) == 0
+
+
 def test_row_split_env_override(tmp_path):
     code = ("import exact_top_selection_amd as e; "
-            "print(e.row_split(4, 262144, 256), e.row_split(64, 32768, 256))")
+            "print(e.row_split(4, 262144, 256, 32), e.row_split(64, 32768, 256, 32), "
+            "e.row_split(4, 262144, 256, 64))")
 
     def run(v):
         env = dict(os.environ, ETS_ROW_SPLIT=v, PYTHONPATH=ROOT)
         return subprocess.run([sys.executable, "-c", code], env=env, capture_output=True,
                               text=True, check=True).stdout.split()
 
-    assert run("7") == ["7", "7"]
-    assert run("0") == ["0", "0"]
-    assert run("1") == ["0", "0"]
-    assert run("1000") == ["32", "32"]
+    assert run("7") == ["7", "7", "7"]
+    assert run("0") == ["0", "0", "0"]
+    assert run("1") == ["0", "0", "0"]
+    assert run("32") == ["32", "32", "32"]
+    # above the device's cap (or the record's 64 slots): rejected, never clamped
+    assert run("64") == ["-1", "-1", "64"]
+    assert run("1000") == ["-1", "-1", "-1"]
 
 
 def test_row_split_heuristic():
@@ -129,29 +161,36 @@ def test_row_split_heuristic():
     try:
         # rows that fit one 32768-score workgroup tile stay whole, whatever the batch
         for B, L in ((64, 32768), (128, 32768), (48, 8192), (1, 2048), (4, 4096), (1024, 8192)):
-            assert ets.row_split(B, L, 256) == 0, (B, L)
+            assert ets.row_split(B, L, 256, 32) == 0, (B, L)
         # longer rows are cut into chunks of about 16384 scores, at most 32
-        assert ets.row_split(4, 32769, 256) == 3
-        assert ets.row_split(4, 65536, 256) == 4
-        assert ets.row_split(2, 100000, 256) == 7
-        assert ets.row_split(4, 262144, 256) == 16
-        assert ets.row_split(16, 262144, 256) == 16
-        assert ets.row_split(1, 10 ** 7, 256) == 32
-        assert ets.row_split(0, 262144, 256) == 0
+        assert ets.row_split(4, 32769, 256, 32) == 3
+        assert ets.row_split(4, 65536, 256, 32) == 4
+        assert ets.row_split(2, 100000, 256, 32) == 7
+        assert ets.row_split(4, 262144, 256, 32) == 16
+        assert ets.row_split(16, 262144, 256, 32) == 16
+        assert ets.row_split(1, 10 ** 7, 256, 32) == 32
+        assert ets.row_split(0, 262144, 256, 32) == 0
         # the grid is held to two workgroups per compute unit ...
-        assert ets.row_split(64, 262144, 256) == 8
-        assert ets.row_split(64, 65536, 256) == 4
-        assert ets.row_split(128, 131072, 256) == 4
+        assert ets.row_split(64, 262144, 256, 32) == 8
+        assert ets.row_split(64, 65536, 256, 32) == 4
+        assert ets.row_split(128, 131072, 256, 32) == 4
         # ... unless that leaves chunks longer than one 32768-score tile ...
-        assert ets.row_split(128, 262144, 256) == 8
-        assert ets.row_split(192, 65536, 256) == 2
-        assert ets.row_split(64, 10 ** 7, 256) == 32
+        assert ets.row_split(128, 262144, 256, 32) == 8
+        assert ets.row_split(192, 131072, 256, 32) == 4
+        # ... but rows of at most two tiles stay whole once B > CUs / 2
+        assert ets.row_split(192, 65536, 256, 32) == 0
+        assert ets.row_split(128, 65536, 256, 32) == 4
+        assert ets.row_split(64, 10 ** 7, 256, 32) == 32
         # ... and rows stay whole once the batch alone fills the device
-        assert ets.row_split(256, 65536, 256) == 0
-        assert ets.row_split(4096, 262144, 256) == 0
+        assert ets.row_split(256, 65536, 256, 32) == 0
+        assert ets.row_split(4096, 262144, 256, 32) == 0
         # an unknown compute-unit count lifts the bound
-        assert ets.row_split(4, 262144, 0) == 16
-        assert ets.row_split(4096, 262144, 0) == 16
+        assert ets.row_split(4, 262144, 0, 32) == 16
+        assert ets.row_split(4096, 262144, 0, 32) == 16
+        # the device's group cap bounds G; an unknown cap leaves the 64 record slots
+        assert ets.row_split(1, 10 ** 7, 256, 20) == 20
+        assert ets.row_split(1, 10 ** 7, 256, 0) == 64
+        assert ets.row_split(1, 10 ** 7, 256, 100) == 64
     finally:
         if env is not None:
             os.environ["ETS_ROW_SPLIT"] = env
@@ -168,7 +207,7 @@ def test_row_split_bounds_hold_everywhere():
         for cu in (80, 256, 304):
             for B in (1, 2, 3, 5, 8, 17, 64, 100, 128, 129, 256, 1000):
                 for L in (1, 32768, 32769, 65536, 100000, 262144, 10 ** 6, 2 ** 31 - 1):
-                    g = ets.row_split(B, L, cu)
+                    g = ets.row_split(B, L, cu, 32)
                     assert 0 <= g <= 32, (cu, B, L, g)
                     if L <= 32768 or B >= cu:
                         assert g == 0, (cu, B, L, g)

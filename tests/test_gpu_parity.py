@@ -347,3 +347,69 @@ def test_variable_windows(overlap):
                               torch.from_numpy(lengths).to(d), k, max_len=int(lengths.max()))
         torch.cuda.synchronize()
         assert_parity(w, out.cpu().numpy(), run_oracle(w))
+
+
+@pytest.mark.parametrize("api", ["raw", "paged"])
+def test_dense_length_clamp_readings(api):
+    """Dense lengths outside [0, L] are clamped on both sides: a negative
+    length selects nothing (all -1), a length above L reads the whole row."""
+    rng = np.random.default_rng(606)
+    B, L, k = 6, 4096, 1024
+    x = rng.standard_normal((B, L)).astype(np.float32)
+    lens = np.array([-1, -5000, L + 1, 2 ** 31 - 1, 0, 2000], dtype=np.int32)
+    pt = np.stack([rng.permutation(L // 64) for _ in range(B)]).astype(np.int32)
+    w = _dense("clamp", api, x, k, lens=lens, pt=pt if api == "paged" else None)
+    got = run_gpu(w)
+    want = run_oracle(w)
+    assert (want[0] == -1).all() and (want[1] == -1).all()
+    assert_parity(w, got, want)
+
+
+def test_ragged_negative_lengths():
+    """A negative ragged length counts as 0: the row is all padding."""
+    rng = np.random.default_rng(607)
+    lengths = np.array([3000, -1, 5000, -70000, 0, 1500], dtype=np.int32)
+    n = np.maximum(lengths, 0)
+    starts = np.zeros_like(lengths)
+    starts[1:] = np.cumsum(n[:-1])
+    packed = rng.standard_normal(int(n.sum()) + 8).astype(np.float32)
+    for k in (1, 1024):
+        w = Workload("ragged-neg", "ragged", k, lengths.size, packed, row_starts=starts,
+                     lengths=lengths)
+        got = run_gpu(w)
+        want = run_oracle(w)
+        assert (want[1] == -1).all() and (want[3] == -1).all()
+        assert_parity(w, got, want)
+
+
+@pytest.mark.parametrize("name", ["C3", "C5"])
+def test_twenty_calls_select_the_same_sets(name):
+    """The same input 20 times on one stream: every call selects the same sets
+    (a split row may order its slots differently), and they are the oracle's."""
+    w = workloads.make(name, seed=46)
+    d = dev()
+    s = torch.from_numpy(w.scores).to(d)
+    out = torch.empty((w.B, w.k), dtype=torch.int32, device=d)
+    if w.api == "paged":
+        lens = torch.from_numpy(w.lens).to(d)
+        pt = torch.from_numpy(w.page_table).to(d)
+        ws = ets.new_workspace(w.B, w.L, w.k, d)
+        call = lambda: ets.topk_paged(s, lens, pt, out, w.page_size, workspace=ws)
+    else:
+        st = torch.from_numpy(w.row_starts).to(d)
+        ln = torch.from_numpy(w.lengths).to(d)
+        ws = ets.new_workspace(w.B, w.max_len, w.k, d)
+        call = lambda: ets.topk_ragged(s, st, ln, w.k, max_len=w.max_len, out=out, workspace=ws)
+    first = None
+    for i in range(20):
+        out.fill_(-3)
+        call()
+        got = np.sort(out.cpu().numpy(), axis=1)
+        if ws is not None:
+            assert ets.workspace_error(ws) == 0
+        if first is None:
+            first = got
+            assert_parity(w, out.cpu().numpy(), run_oracle(w))
+        else:
+            bad = np.nonzero((got != first).any(axis=1))[0]
+            assert bad.size == 0, "call %d: %d rows differ from the first call" % (i, bad.size)

@@ -52,7 +52,25 @@ def _cached_workspaces():
     return [w for w in ets._ws_cache.values()]
 
 
-@pytest.mark.parametrize("g", [2, 3, 8, 17, 32])
+@pytest.fixture(autouse=True)
+def _error_words_stay_zero():
+    """After every test: no call on the implicit workspaces stopped waiting for
+    its row group (the error word, read and cleared through the C ABI)."""
+    for ws in _cached_workspaces():
+        ets.workspace_error(ws)
+    yield
+    for ws in _cached_workspaces():
+        assert ets.workspace_error(ws) == 0, "a call stopped waiting for its row group"
+
+
+_G64 = pytest.param(64, marks=pytest.mark.skip(
+    reason="64 members per row exceed one XCD's 32 row-group slots on MI355X: a ticketed "
+           "grid can then stall until the bounded waits expire (seen on a 4096-workgroup "
+           "grid; tests/test_dispatch_model.py models it); the library rejects G above "
+           "the device's cap"))
+
+
+@pytest.mark.parametrize("g", [2, 3, 8, 17, 32, _G64])
 @pytest.mark.parametrize("name", ["C2", "C3"])
 def test_forced_split_matches_single(name, g):
     w = workloads.make(name, seed=45)
@@ -134,7 +152,7 @@ def test_split_short_rows_and_empty_chunks():
     lens = np.array([0, 1, k - 1, k, k + 1, k + 3, 2 * k, 4100, L], dtype=np.int32)
     x = rng.standard_normal((lens.size, L)).astype(np.float32)
     w = _raw("short-split", x, k, lens)
-    for g in (2, 17, 64):
+    for g in (2, 17, 32):
         with split(g):
             assert_parity(w, run_gpu(w), run_oracle(w))
 
@@ -303,3 +321,122 @@ def test_banded_and_narrow_rows(kind, g):
             assert_parity(w, run_gpu(w), run_oracle(w))
     for ws in _cached_workspaces():
         _assert_clean(ws)
+
+
+def test_split_override_above_cap_is_rejected():
+    """ETS_ROW_SPLIT above the device's row-group cap is an argument error,
+    reported before anything is enqueued, never a silent clamp."""
+    cu, xcd, cap = ets.device_limits()
+    assert cap == ets.group_cap(cu, xcd, 1) or cap >= 2
+    d = dev()
+    x = torch.zeros((2, 65536), dtype=torch.float32, device=d)
+    with split(cap + 1):
+        assert ets.row_split(2, 65536, cu, cap) == -1
+        with pytest.raises(ets.EtsError) as e:
+            ets.topk_raw(x, 64)
+        assert e.value.status == 1
+        with pytest.raises(ets.EtsError):
+            ets.workspace_size(2, 65536, 64)
+    with split(cap):
+        out = ets.topk_raw(x, 64)
+        torch.cuda.synchronize()
+        assert out.shape == (2, 64)
+
+
+@pytest.mark.parametrize("B,L,k", [(128, 262144, 2048), (192, 131072, 1024), (192, 65536, 1024)])
+def test_default_heuristic_large_batches(B, L, k):
+    """The heuristic's choices for long rows at large batches: chunks of 32768
+    scores held in registers on a ticketed grid (B = 128, L = 262144: G = 8;
+    B = 192, L = 131072: G = 4) and whole streamed rows (B = 192, L = 65536)."""
+    cu, _, cap = ets.device_limits()
+    print("case default B", B, "L", L, "G", ets.row_split(B, L, cu, cap), flush=True)
+    rng = np.random.Generator(np.random.PCG64(B * 7 + L))
+    x = workloads.normal_dense(rng, B, L)
+    lens = rng.integers(L // 2, L, size=B, endpoint=True).astype(np.int32)
+    w = _raw("default-large", x, k, lens)
+    d = dev()
+    ws = ets.new_workspace(B, L, k, d)
+    out = torch.full((B, k), 5, dtype=torch.int32, device=d)
+    ets.topk_raw(torch.from_numpy(x).to(d), k, torch.from_numpy(lens).to(d), out=out, workspace=ws)
+    if ws is not None:
+        assert ets.workspace_error(ws) == 0
+    assert_parity(w, out.cpu().numpy(), run_oracle(w))
+    if ws is not None:
+        _assert_clean(ws)
+
+
+@pytest.mark.parametrize("api", ["raw", "paged"])
+@pytest.mark.parametrize("g,L", [(3, 65536), (2, 60000), (5, 131072)])
+def test_forced_split_resident_chunks_above_16384(api, g, L):
+    """Chunks of 16385 to 32768 scores: each member holds 32 keys per lane."""
+    rng = np.random.Generator(np.random.PCG64(g * 100 + L % 97))
+    B, k, ps = 4, 1024, 64
+    x = workloads.normal_dense(rng, B, L)
+    lens = np.array([L, L - 1, L // 2 + 3, 33000], dtype=np.int32)
+    if api == "raw":
+        w = _raw("chunks-big", x, k, lens)
+    else:
+        pt = np.stack([rng.permutation(-(-L // ps)) for _ in range(B)]).astype(np.int32)
+        w = Workload("chunks-big-paged", "paged", k, B, x, L=L, lens=lens, page_table=pt,
+                     page_size=ps)
+    print("case", api, "G", g, "L", L, flush=True)
+    with split(g):
+        assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+@pytest.mark.parametrize("g", [4, 5])
+def test_split_k2_one_score_tail_chunk(g):
+    """k = 2 with a member whose chunk holds one score (a 49-score row at G = 4:
+    chunks of 16, 16, 16 and 1): such a chunk offers no lower bound."""
+    rng = np.random.default_rng(9)
+    L = 52
+    lens = np.array([49, 45, 33, 52, 3, 17], dtype=np.int32)
+    x = rng.standard_normal((lens.size, L)).astype(np.float32)
+    x[1, 44] = 50.0  # the only score of its member's chunk is the row's largest
+    for k in (1, 2, 3):
+        w = _raw("tail-one", x, k, lens)
+        with split(g):
+            assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+def test_workspace_error_word_is_copied_and_cleared():
+    """ets_workspace_error copies the word into a caller buffer on the stream
+    and clears it; a call that needed no workspace reports 0."""
+    d = dev()
+    ws = ets.new_workspace(4, 262144, 2048, d)
+    flag = torch.full((1,), -1, dtype=torch.int32, device=d)
+    ets.workspace_error_async(ws, flag)
+    torch.cuda.synchronize()
+    assert flag.item() == 0
+    ws.view(torch.int32)[32] = 7  # planted from the host
+    ets.workspace_error_async(ws, flag)
+    torch.cuda.synchronize()
+    assert flag.item() == 7
+    assert int(ws.view(torch.int32)[32].item()) == 0
+    ets.workspace_error_async(None, flag)
+    torch.cuda.synchronize()
+    assert flag.item() == 0
+
+
+def test_stale_ticket_sets_the_error_word():
+    """A ticketed grid on a workspace whose ticket counter is not zero (a
+    planted stale value): every workgroup finds no row, ends at once and the
+    error word says so; the last one re-arms the counter, so the next call on
+    the same workspace is exact again."""
+    d = dev()
+    cu, _, cap = ets.device_limits()
+    B, L, k = 64, 131072, 2048
+    G = ets.row_split(B, L, cu, cap)
+    assert G * B > cu, "needs a ticketed grid"
+    x = workloads.normal_dense(np.random.Generator(np.random.PCG64(3)), B, L)
+    s = torch.from_numpy(x).to(d)
+    ws = ets.new_workspace(B, L, k, d)
+    ws.view(torch.int32)[0] = 1 << 30  # stale ticket
+    out = torch.full((B, k), 7, dtype=torch.int32, device=d)
+    ets.topk_raw(s, k, out=out, workspace=ws)
+    assert ets.workspace_error(ws) == 2
+    assert int(torch.count_nonzero(out != 7).item()) == 0  # nothing was selected
+    _assert_clean(ws)
+    ets.topk_raw(s, k, out=out, workspace=ws)
+    assert ets.workspace_error(ws) == 0
+    assert_parity(_raw("after-stale", x, k), out.cpu().numpy(), run_oracle(_raw("after-stale", x, k)))
