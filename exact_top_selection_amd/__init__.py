@@ -26,7 +26,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["topk_raw", "topk_paged", "topk_ragged", "workspace_size", "row_split", "floor_read",
+__all__ = ["topk_raw", "topk_paged", "topk_ragged", "topk_paged_noalloc", "workspace_size", "row_split", "floor_read",
            "floor_launch", "device_limits", "group_cap",
            "new_workspace", "workspace_init", "workspace_error", "workspace_error_async",
            "library_path", "MAX_K", "EtsError"]
@@ -64,6 +64,8 @@ def _load():
             lib.ets_topk_paged.argtypes = [vp, i64, i32, i32, vp, vp, i64, i32, i32, vp, i64,
                                            vp, sz, vp]
             lib.ets_topk_ragged.argtypes = [vp, vp, vp, i32, i64, i32, vp, i64, vp, sz, vp]
+            lib.ets_topk_paged_noalloc.argtypes = [vp, i64, i32, i32, vp, vp, i64, i32, i32, vp,
+                                                   i64, vp, vp]
             lib.ets_workspace_size.argtypes = [i32, i64, i32, i32, ctypes.POINTER(sz)]
             lib.ets_row_split.argtypes = [i32, i64, i32, i32]
             lib.ets_workspace_init.argtypes = [vp, sz, vp]
@@ -75,6 +77,7 @@ def _load():
             lib.ets_floor_read.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp, i64, vp]
             lib.ets_floor_launch.argtypes = [i32, i64, vp]
             for fn in (lib.ets_topk_raw, lib.ets_topk_paged, lib.ets_topk_ragged,
+                       lib.ets_topk_paged_noalloc,
                        lib.ets_workspace_size, lib.ets_row_split, lib.ets_workspace_init,
                        lib.ets_workspace_error, lib.ets_device_limits, lib.ets_group_cap,
                        lib.ets_floor_read, lib.ets_floor_launch):
@@ -310,6 +313,46 @@ def topk_paged(scores: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.T
                                     ws.data_ptr() if ws is not None else None, ws_bytes,
                                     _stream(dev))
     _check(st, "ets_topk_paged")
+    return out
+
+
+def topk_paged_noalloc(scores: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.Tensor,
+                       page_indices: torch.Tensor, page_size: int,
+                       error_flag: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``topk_paged`` without a workspace: split rows use the library's static
+    per-device scratch (4 MiB), so the call allocates nothing, here or in the
+    library.  Calls that may overlap on one device race.  ``error_flag``
+    (int32 [>=1], optional) receives the scratch's error word."""
+    _require(scores, "scores", torch.float32, 2)
+    B, L = scores.shape
+    dev = scores.device
+    _vec(seq_lens, "seq_lens", B)
+    _require(page_table, "page_table", torch.int32, 2)
+    if page_table.shape[0] != B:
+        raise ValueError("page_table must have B rows")
+    _require(page_indices, "page_indices", torch.int32, 2)
+    k = page_indices.shape[1]
+    out = _out(page_indices, B, k, dev)
+    for t, nm in ((seq_lens, "seq_lens"), (page_table, "page_table")):
+        if t.device != dev:
+            raise ValueError("%s must be on %s" % (nm, dev))
+    if page_size < 1:
+        raise ValueError("page_size must be >= 1")
+    if page_table.shape[1] * page_size < L:
+        raise ValueError("page_table has %d pages of %d, fewer than L = %d positions"
+                         % (page_table.shape[1], page_size, L))
+    if error_flag is not None:
+        _require(error_flag, "error_flag", torch.int32, 1)
+        if error_flag.device != dev or error_flag.numel() < 1:
+            raise ValueError("error_flag must be int32 [>=1] on %s" % dev)
+    with torch.cuda.device(dev):
+        st = _load().ets_topk_paged_noalloc(scores.data_ptr(), _rows(scores, "scores"), B, L,
+                                            seq_lens.data_ptr(), page_table.data_ptr(),
+                                            _rows(page_table, "page_table"), page_size, k,
+                                            out.data_ptr(), out.stride(0) if B > 1 else k,
+                                            error_flag.data_ptr() if error_flag is not None
+                                            else None, _stream(dev))
+    _check(st, "ets_topk_paged_noalloc")
     return out
 
 

@@ -1980,6 +1980,27 @@ __global__ __launch_bounds__(T) void floor_read_kernel(Params p, uint32_t* sink,
 template <int T>
 __global__ __launch_bounds__(T) void floor_launch_kernel() {}
 
+// Row-group workspace for callers that cannot allocate (ets_topk_paged_noalloc):
+// static device storage of kScratchBytes, one copy per device, held until
+// the process ends.  Host code never uses this name as an address: it takes
+// the device address once per device with hipGetSymbolAddress.
+constexpr size_t kScratchBytes = ETS_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "whole 256-byte lines");
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / 4];
+
+// Copies the error word of workspace ws (words) to flag[0]; if it is set,
+// zero-fills the whole workspace so that the next call starts clean.
+__global__ __launch_bounds__(1024) void scratch_error_take(uint32_t* ws, int64_t words, int32_t* flag) {
+  __shared__ uint32_t e;
+  if (threadIdx.x == 0) {
+    e = ld_dev(ws + kHdrError);
+    flag[0] = static_cast<int32_t>(e);
+  }
+  __syncthreads();
+  if (e == 0) return;
+  for (int64_t i = threadIdx.x; i < words; i += 1024) st_dev(ws + i, 0u);
+}
+
 }  // namespace ets
 
 // ==================================================================== host side
@@ -2235,6 +2256,37 @@ ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, const Device
   return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
 }
 
+// Per-device address of ets::scratch (hipGetSymbolAddress once per device,
+// with that device current) and whether it has been zero-filled by a launch
+// that ran outside graph capture.
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_zeroed[kMaxDevices] = {};
+
+ets_status scratch_setup(int dev, hipStream_t stream, void** ptr_out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(ets::scratch)) != hipSuccess || ptr == nullptr)
+      return ETS_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  if (!g_scratch_zeroed[dev]) {
+    // zero-fill on the caller's stream with a kernel (no memset node if the
+    // stream is being captured: the graph then zero-fills on every replay
+    // until an eager call has done it once)
+    const int64_t words = static_cast<int64_t>(ets::kScratchBytes / 4);
+    hipLaunchKernelGGL(ets::workspace_clear, dim3(1024), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(g_scratch_ptr[dev]), words);
+    if (hipGetLastError() != hipSuccess) return ETS_ERR_HIP;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return ETS_ERR_HIP;
+    if (cs == hipStreamCaptureStatusNone) g_scratch_zeroed[dev] = true;
+  }
+  *ptr_out = g_scratch_ptr[dev];
+  return ETS_OK;
+}
+
 template <int MODE, bool V4, int T, int VEC>
 void launch_floor_read(const ets::Params& p, uint32_t grid, uint32_t* sink, int32_t G, hipStream_t s) {
   hipLaunchKernelGGL((ets::floor_read_kernel<T, VEC, MODE, V4>), dim3(grid), dim3(T), 0, s, p, sink, G);
@@ -2320,6 +2372,7 @@ const char* ets_status_string(ets_status status) {
     case ETS_ERR_WORKSPACE: return "workspace too small";
     case ETS_ERR_DEVICE: return "unsupported or unavailable device (gfx950 required)";
     case ETS_ERR_HIP: return "HIP runtime error";
+    case ETS_ERR_SCRATCH: return "call needs more row-group workspace than the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -2436,6 +2489,48 @@ ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, in
   auto s = static_cast<hipStream_t>(stream);
   return v4 ? launch<ets::kPaged, true>(p, B, L, info, workspace, s)
             : launch<ets::kPaged, false>(p, B, L, info, workspace, s);
+}
+
+ets_status ets_topk_paged_noalloc(const float* scores, int64_t row_stride, int32_t B, int32_t L,
+                                  const int32_t* seq_lens, const int32_t* page_table,
+                                  int64_t pt_stride, int32_t page_size, int32_t k, int32_t* out,
+                                  int64_t out_stride, int32_t* error_flag, void* stream) {
+  if (k < 1 || k > ETS_MAX_K) return ETS_ERR_K_RANGE;
+  if (B < 0 || L < 0 || row_stride < L || out_stride < k || page_size < 1 || pt_stride < 0)
+    return ETS_ERR_INVALID_ARG;
+  if (B == 0) return ETS_OK;
+  if (!out || !seq_lens || !page_table || (L > 0 && !scores)) return ETS_ERR_INVALID_ARG;
+  int dev;
+  DeviceInfo info;
+  if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
+  const int32_t G = split_plan(B, L, info.cu_count, info.group_cap);
+  if (G < 0 || static_cast<int64_t>(B) * G > INT32_MAX) return ETS_ERR_INVALID_ARG;
+  const size_t need = G == 0 ? 0 : group_ws_bytes(B);
+  if (need > ets::kScratchBytes) return ETS_ERR_SCRATCH;
+  auto s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (need > 0 || error_flag != nullptr) {
+    if (ets_status st = scratch_setup(dev, s, &ws); st != ETS_OK) return st;
+  }
+  ets::Params p{};
+  p.scores = scores;
+  p.row_stride = row_stride;
+  p.lens = seq_lens;
+  p.page_table = page_table;
+  p.pt_stride = pt_stride;
+  p.page_size = page_size;
+  p.page_shift = page_shift_of(page_size);
+  p.L = L;
+  p.k = k;
+  p.out = out;
+  p.out_stride = out_stride;
+  const bool v4 = aligned16(scores) && (row_stride % 4 == 0) && (L % 4 == 0);
+  const ets_status st = v4 ? launch<ets::kPaged, true>(p, B, L, info, ws, s)
+                           : launch<ets::kPaged, false>(p, B, L, info, ws, s);
+  if (st != ETS_OK || error_flag == nullptr) return st;
+  hipLaunchKernelGGL(ets::scratch_error_take, dim3(1), dim3(1024), 0, s, static_cast<uint32_t*>(ws),
+                     static_cast<int64_t>(ets::kScratchBytes / 4), error_flag);
+  return hipGetLastError() == hipSuccess ? ETS_OK : ETS_ERR_HIP;
 }
 
 ets_status ets_topk_ragged(const float* packed, const int32_t* row_starts,

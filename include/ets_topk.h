@@ -73,6 +73,7 @@ typedef int32_t ets_status;
 #define ETS_ERR_WORKSPACE 3   /* workspace smaller than ets_workspace_size() */
 #define ETS_ERR_DEVICE 4      /* current device is not gfx950 or cannot be queried */
 #define ETS_ERR_HIP 5         /* a HIP launch or runtime call failed */
+#define ETS_ERR_SCRATCH 6     /* ets_topk_paged_noalloc: the call needs more than its static scratch */
 
 /* Largest supported k (the pages fix k at 1024 for the paged transform,
  * PR #36004 digest, kMaxTopK excerpt, and at 2048 for the DSA top-k,
@@ -109,6 +110,35 @@ ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, in
                           const int32_t* seq_lens, const int32_t* page_table, int64_t pt_stride,
                           int32_t page_size, int32_t k, int32_t* out, int64_t out_stride,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the paged
+ * call above with the same arguments and results, but with no workspace
+ * argument.  Calls whose rows split over row groups use a static device
+ * array of ETS_NOALLOC_SCRATCH_BYTES (4 MiB, one per device, held until the
+ * process ends) instead; nothing is allocated or freed, and no memset node is
+ * recorded.  A call whose plan needs more workspace than that (a split call
+ * with B above 50 on MI355X) returns ETS_ERR_SCRATCH before enqueueing
+ * anything; calls that keep one workgroup per row need none and take any B.
+ *   - The first call on a device zero-fills the array on `stream` with a
+ *     kernel (inside a graph being captured, every replay does, until a call
+ *     outside capture has done it once); every call returns the array's
+ *     counters and tables to zero.
+ *   - All calls on one device share the array: calls that may overlap (on
+ *     different streams, or graphs replayed concurrently) race and their
+ *     results are undefined.  Serialise them on one stream.
+ *   - error_flag (nullable, device int32, caller-owned): when given, the call
+ *     also copies the array's error word into error_flag[0] on `stream`
+ *     (non-zero: a row group stopped waiting and this call's output is
+ *     undefined; see ets_workspace_error) and, if it is set, zero-fills the
+ *     array so that the next call starts clean.
+ */
+#define ETS_NOALLOC_SCRATCH_BYTES (4u << 20)
+ets_status ets_topk_paged_noalloc(const float* scores, int64_t row_stride, int32_t B, int32_t L,
+                                  const int32_t* seq_lens, const int32_t* page_table,
+                                  int64_t pt_stride, int32_t page_size, int32_t k, int32_t* out,
+                                  int64_t out_stride, int32_t* error_flag, void* stream);
 
 /*
  * Packed ragged rows (PR #37591 digest, CoopParams excerpt: row_starts and
