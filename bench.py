@@ -8,6 +8,10 @@ least 512 MiB, so the 256 MiB last-level cache cannot serve the scores.
 
 Prints one JSON line: rows/s (value) plus effective HBM GB/s against the
 8 TB/s peak (roofline) and the CPU oracle's rows/s on the host (cpu_baseline).
+After the headline workload (C3 by default), every named workload C1 .. C5 is
+timed the same way over max(K, 200) calls (per_config), each with its empty
+launch and read-only floors; none of that is inside the headline's timed
+region.
 """
 from __future__ import annotations
 
@@ -224,6 +228,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-floors", action="store_true",
                     help="skip the empty-launch and read-only floors")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload lines (C1 .. C5) after the headline")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -250,50 +256,19 @@ def main() -> int:
     if args.calibrate_copy:
         return calibrate_copy(torch, args.steps)
 
-    w = workloads.make(args.workload, seed=args.seed)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    # ---- ring of input copies (>= 512 MiB) resident in HBM
-    per_copy = w.scores.nbytes
-    R = max(1, -(-RING_BYTES // per_copy))
-    scores0 = torch.from_numpy(w.scores).to(dev)
-    ring = torch.empty((R,) + tuple(scores0.shape), dtype=torch.float32, device=dev)
-    ring.copy_(scores0.unsqueeze(0).expand_as(ring))
-    del scores0
-    out = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
-    # one zero-filled workspace for every step (each call leaves it zero)
-    ws = ets.new_workspace(w.B, w.max_len if w.api == "ragged" else w.L, w.k, dev)
-    if w.api == "paged":
-        lens = torch.from_numpy(w.lens).to(dev)
-        pt = torch.from_numpy(w.page_table).to(dev)
-
-        def step(i):
-            ets.topk_paged(ring[i % R], lens, pt, out, w.page_size, workspace=ws)
-    elif w.api == "raw":
-        lens = torch.from_numpy(w.lens).to(dev) if w.lens is not None else None
-
-        def step(i):
-            ets.topk_raw(ring[i % R], w.k, lens, out=out, workspace=ws)
-    else:
-        starts = torch.from_numpy(w.row_starts).to(dev)
-        lengths = torch.from_numpy(w.lengths).to(dev)
-        max_len = w.max_len
-
-        def step(i):
-            ets.topk_ragged(ring[i % R], starts, lengths, w.k, max_len=max_len, out=out,
-                            workspace=ws)
-
-    ms_total = timed(torch, step, args.steps, args.warmup, args.eager)
-    ms_per_step = ms_total / args.steps
-    rows_per_s = w.B / (ms_per_step * 1e-3)
-    abytes = algorithmic_bytes(w)
-    achieved = abytes / (ms_per_step * 1e-3) / 1e9  # GB/s; one kernel launch per step
-
-    # the one kernel a step launches: one workgroup per row, or row groups
     cu, _, cap = ets.device_limits()
-    split = ets.row_split(w.B, w.max_len if w.api == "ragged" else w.L, cu, cap)
-    kernel = "group_topk_kernel (%d workgroups per row)" % split if split else "row_topk_kernel"
+    aux_steps = max(args.steps, 200)  # floors and per-config lines
+
+    # ---- the headline workload
+    w = workloads.make(args.workload, seed=args.seed)
+    rig = Rig(torch, ets, w, dev, cu, cap)
+    ms_total = timed(torch, rig.step, args.steps, args.warmup, args.eager)
+    us_per_step = ms_total * 1e3 / args.steps
+    rows_per_s = w.B / (us_per_step * 1e-6)
+    abytes = algorithmic_bytes(w)
+    achieved = abytes / (us_per_step * 1e-6) / 1e9  # GB/s; one kernel launch per step
     result = {
         "metric": METRIC,
         "value": rows_per_s,
@@ -301,7 +276,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": us_per_step * 1e-3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -311,7 +286,7 @@ def main() -> int:
             "workload": "%s: %s" % (w.name, w.note),
             "api": w.api, "B": w.B, "L": int(w.L or w.max_len), "k": w.k,
             "page_size": w.page_size or None, "seed": args.seed,
-            "input_ring_copies": R,
+            "input_ring_copies": rig.R,
             "launch": "eager launches" if args.eager else "hip graph of K steps",
             "algorithmic_bytes_per_step": abytes,
         },
@@ -322,36 +297,106 @@ def main() -> int:
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(w.name),
-            "kernel": kernel,
-            "kernel_us_per_launch": ms_per_step * 1e3,
+            "kernel": rig.kernel,
+            # one kernel per step: HIP events on the launching stream around the
+            # K replayed steps, divided by K
+            "us_per_launch": us_per_step,
         },
     }
     if not args.no_floors:
-        # the same grid with empty workgroups, and the same reads with nothing
-        # selected, timed the same way over the same input ring
-        max_len = w.max_len if w.api == "ragged" else w.L
-        sink = torch.empty(w.B * max(1, split), dtype=torch.int32, device=dev)
-        if w.api == "ragged":
-            def read_step(i):
-                ets.floor_read(ring[i % R], lengths, starts, max_len, sink=sink)
-        else:
-            def read_step(i):
-                ets.floor_read(ring[i % R], lens, sink=sink)
+        result["floors"] = rig.floors(aux_steps, args.warmup, args.eager)
+    del rig
+    torch.cuda.empty_cache()
 
-        def launch_step(i):
-            ets.floor_launch(w.B, max_len, dev)
-        result["floors"] = {
-            "launch_us": timed(torch, launch_step, args.steps, args.warmup, args.eager)
-            * 1e3 / args.steps,
-            "read_us": timed(torch, read_step, args.steps, args.warmup, args.eager)
-            * 1e3 / args.steps,
-            "what": "per call: an empty launch of the same grid; the same grid reading "
-                    "the same bytes and forming keys, one max per workgroup",
-        }
+    # ---- every workload, timed the same way (outside the headline's timed region)
+    if not args.no_configs:
+        per = {}
+        for name in workloads.NAMES:
+            wc = workloads.make(name, seed=args.seed)
+            rc = Rig(torch, ets, wc, dev, cu, cap)
+            us = timed(torch, rc.step, aux_steps, args.warmup, args.eager) * 1e3 / aux_steps
+            ab = algorithmic_bytes(wc)
+            gbs = ab / (us * 1e-6) / 1e9
+            per[name] = {"us_per_call": us, "rows_per_s": wc.B / (us * 1e-6), "gb_per_s": gbs,
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": ab,
+                         "kernel": rc.kernel, "calls": aux_steps}
+            if not args.no_floors:
+                per[name]["floors"] = rc.floors(aux_steps, args.warmup, args.eager)
+            del rc
+            torch.cuda.empty_cache()
+        result["per_config"] = per
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
+
+
+class Rig:
+    """One workload's inputs resident in HBM as a ring of copies (>= 512 MiB,
+    so the 256 MiB last-level cache cannot serve the scores), its output and
+    workspace, and one step = one call on copy i % R."""
+
+    def __init__(self, torch, ets, w, dev, cu, cap):
+        self.w, self.dev, self.torch, self.ets = w, dev, torch, ets
+        per_copy = w.scores.nbytes
+        self.R = R = max(1, -(-RING_BYTES // per_copy))
+        scores0 = torch.from_numpy(w.scores).to(dev)
+        self.ring = ring = torch.empty((R,) + tuple(scores0.shape), dtype=torch.float32, device=dev)
+        ring.copy_(scores0.unsqueeze(0).expand_as(ring))
+        del scores0
+        self.out = out = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+        self.max_len = w.max_len if w.api == "ragged" else w.L
+        # one zero-filled workspace for every step (each call leaves it zero)
+        self.ws = ws = ets.new_workspace(w.B, self.max_len, w.k, dev)
+        self.split = ets.row_split(w.B, self.max_len, cu, cap)
+        self.kernel = ("group_topk_kernel (%d workgroups per row)" % self.split if self.split
+                       else "row_topk_kernel")
+        if w.api == "paged":
+            self.lens = lens = torch.from_numpy(w.lens).to(dev)
+            pt = torch.from_numpy(w.page_table).to(dev)
+
+            def step(i):
+                ets.topk_paged(ring[i % R], lens, pt, out, w.page_size, workspace=ws)
+        elif w.api == "raw":
+            self.lens = lens = torch.from_numpy(w.lens).to(dev) if w.lens is not None else None
+
+            def step(i):
+                ets.topk_raw(ring[i % R], w.k, lens, out=out, workspace=ws)
+        else:
+            self.starts = starts = torch.from_numpy(w.row_starts).to(dev)
+            self.lens = lengths = torch.from_numpy(w.lengths).to(dev)
+            max_len = w.max_len
+
+            def step(i):
+                ets.topk_ragged(ring[i % R], starts, lengths, w.k, max_len=max_len, out=out,
+                                workspace=ws)
+        self.step = step
+
+    def floors(self, steps, warmup, eager):
+        """Per call: the same grid launched empty, and the same grid reading the
+        same bytes and forming keys (one max per workgroup), timed the same way
+        over the same input ring."""
+        torch, ets, w, R, ring = self.torch, self.ets, self.w, self.R, self.ring
+        sink = torch.empty(w.B * max(1, self.split), dtype=torch.int32, device=self.dev)
+        if w.api == "ragged":
+            starts, lengths, max_len = self.starts, self.lens, self.max_len
+
+            def read_step(i):
+                ets.floor_read(ring[i % R], lengths, starts, max_len, sink=sink)
+        else:
+            lens = self.lens
+
+            def read_step(i):
+                ets.floor_read(ring[i % R], lens, sink=sink)
+        dev, B, max_len = self.dev, w.B, self.max_len
+
+        def launch_step(i):
+            ets.floor_launch(B, max_len, dev)
+        return {"launch_us": timed(torch, launch_step, steps, warmup, eager) * 1e3 / steps,
+                "read_us": timed(torch, read_step, steps, warmup, eager) * 1e3 / steps,
+                "calls": steps,
+                "what": "per call: an empty launch of the same grid; the same grid reading "
+                        "the same bytes and forming keys, one max per workgroup"}
 
 
 if __name__ == "__main__":

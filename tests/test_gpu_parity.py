@@ -413,3 +413,41 @@ def test_twenty_calls_select_the_same_sets(name):
         else:
             bad = np.nonzero((got != first).any(axis=1))[0]
             assert bad.size == 0, "call %d: %d rows differ from the first call" % (i, bad.size)
+
+
+def _ordered_rows(rng, kind, B, L):
+    x = rng.standard_normal((B, L)).astype(np.float32)
+    if kind == "ascending":
+        x = np.sort(x, axis=1)
+    elif kind == "descending":
+        x = -np.sort(x, axis=1)
+    elif kind == "late-max":
+        # the float4 groups of the first 8 waves of a 1024-lane workgroup
+        # (positions 4 (v T + t), t < 512) hold small scores only, so the
+        # bounds taken from those waves are far below the threshold
+        idx = np.arange(L)
+        first = ((idx // 4) % 1024) < 512
+        x[:, first] = x[:, first] * 0.25 - 3.0
+    elif kind == "ties":
+        x = rng.integers(-40, 40, size=(B, L)).astype(np.float32) / 8
+    return x
+
+
+@pytest.mark.parametrize("kind", ["normal", "ascending", "descending", "late-max", "ties"])
+@pytest.mark.parametrize("L", [16384, 32768])
+def test_long_rows_by_score_order(kind, L):
+    """Long rows whose scores are sorted either way, whose largest scores all
+    sit away from the waves whose loads land first, or that hold few distinct
+    values, at lengths from just above 8k to the full tile."""
+    kinds = ["normal", "ascending", "descending", "late-max", "ties"]
+    rng = np.random.default_rng(1000 * kinds.index(kind) + L)
+    B = 8
+    x = _ordered_rows(rng, kind, B, L)
+    lens = np.array([L, L - 1, L - 3, 3 * L // 4 + 1, L // 2, L // 2 - 5, 8193, 8192],
+                    dtype=np.int32)
+    for k in (1, 2, 64, 500, 1024):
+        for api in ("raw", "paged"):
+            print("case ordered", kind, "L", L, "k", k, api, flush=True)
+            w = _dense("ordered", api, x, k, lens=lens,
+                       pt=np.stack([rng.permutation(L // 64) for _ in range(B)]) if api == "paged" else None)
+            assert_parity(w, run_gpu(w), run_oracle(w))
