@@ -230,6 +230,11 @@ def main() -> int:
                     help="skip the empty-launch and read-only floors")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload lines (C1 .. C5) after the headline")
+    ap.add_argument("--sweep", choices=["batch", "k"],
+                    help="instead of the headline: one JSON line per point of a sweep, "
+                         "'batch' = paged decode rows of 32768 scores, k = 1024, B in "
+                         "1 .. 512 (HIP graph and eager launches); 'k' = the C3 workload with "
+                         "k in 1 .. 2048")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -255,6 +260,8 @@ def main() -> int:
 
     if args.calibrate_copy:
         return calibrate_copy(torch, args.steps)
+    if args.sweep:
+        return sweep(torch, ets, workloads, args)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -328,6 +335,46 @@ def main() -> int:
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def sweep(torch, ets, workloads, args) -> int:
+    """Latency against batch size (the decode caller's flat region) or against k."""
+    from workloads import Workload
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cu, _, cap = ets.device_limits()
+    steps = max(args.steps, 200)
+    points = []
+    if args.sweep == "batch":
+        L, k, ps = 32768, 1024, 64
+        for B in (1, 8, 32, 64, 128, 256, 512):
+            rng = np.random.Generator(np.random.PCG64(args.seed + B))
+            x = workloads.normal_dense(rng, B, L)
+            pt = np.stack([rng.permutation(L // ps) for _ in range(B)]).astype(np.int32)
+            w = Workload("decode-B%d" % B, "paged", k, B, x, L=L,
+                         lens=np.full(B, L, dtype=np.int32), page_table=pt, page_size=ps,
+                         note="paged, seq_lens all %d, k %d, N(0,1)" % (L, k))
+            points.append(w)
+    else:
+        base = workloads.make("C3", seed=args.seed)
+        for k in (1, 64, 256, 512, 1024, 2048):
+            points.append(Workload("C3-k%d" % k, "paged", k, base.B, base.scores, L=base.L,
+                                   lens=base.lens, page_table=base.page_table,
+                                   page_size=base.page_size, note=base.note))
+    for w in points:
+        rig = Rig(torch, ets, w, dev, cu, cap)
+        us_g = timed(torch, rig.step, steps, args.warmup, False) * 1e3 / steps
+        us_e = timed(torch, rig.step, steps, args.warmup, True) * 1e3 / steps
+        ab = algorithmic_bytes(w)
+        print(json.dumps({"point": w.name, "B": w.B, "k": w.k, "L": w.L,
+                          "us_per_call_graph": us_g, "us_per_call_eager": us_e,
+                          "rows_per_s": w.B / (us_g * 1e-6), "gb_per_s": ab / (us_g * 1e-6) / 1e9,
+                          "frac": ab / (us_g * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                          "algorithmic_bytes": ab, "kernel": rig.kernel, "calls": steps}),
+              flush=True)
+        del rig
+        torch.cuda.empty_cache()
     return 0
 
 

@@ -1263,11 +1263,14 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // the tables to zero (tie lists may keep stale entries).
 
 constexpr int kTieCap = 4096;      // tie-list entries per row
-// Round 0 exchanges 2^kCoarseBits bins per row.  Measured on MI355X for rows
-// of 65536 to 262144 scores: 256 bins beat 64 (larger tie lists) and 1024
-// (more device atomics), and packed bins beat bins spread over more lines;
-// 512 bins help N(0,1) rows of 131072 and more but not banded ones.
-constexpr int kCoarseBits = 8;
+// Round 0 exchanges 2^kCoarseBits bins per row.  Measured on MI355X (HIP
+// graph of 300 calls): 512 bins against 256 cut the banded ragged rows of
+// 65536 to 262144 scores (B = 4, k = 2048) from 14.97 to 14.10 us, and N(0,1)
+// rows at B = 1, L = 262144 and B = 4, L = 65536 by about 1 us, with B = 16
+// and 64 unchanged: the threshold's coarse bin then holds under 128 scores,
+// so the last member ranks the tie list directly; 1024 bins cost 6 to 12 us
+// more on the N(0,1) rows (more device atomics and a longer poll).
+constexpr int kCoarseBits = 9;
 constexpr int kCoarseBins = 1 << kCoarseBits;
 constexpr int kFinePerCoarse = kHistBins / kCoarseBins;
 constexpr int kGroupPtCap = 1024;  // chunk page-table entries staged in LDS

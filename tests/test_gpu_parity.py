@@ -451,3 +451,28 @@ def test_long_rows_by_score_order(kind, L):
             w = _dense("ordered", api, x, k, lens=lens,
                        pt=np.stack([rng.permutation(L // 64) for _ in range(B)]) if api == "paged" else None)
             assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+@pytest.mark.parametrize("k", [1, 64, 256, 512, 1024, 2048])
+def test_k_sweep_on_c3(k):
+    """Runtime k over its range on the C3 shape (paged, B = 64, seq_lens up
+    to 32768), the k sweep of the measurement."""
+    base = workloads.make("C3", seed=47)
+    w = Workload("C3-k%d" % k, "paged", k, base.B, base.scores, L=base.L, lens=base.lens,
+                 page_table=base.page_table, page_size=base.page_size)
+    print("case C3 k", k, flush=True)
+    assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+@pytest.mark.parametrize("B", [1, 8, 256, 512])
+def test_decode_batches(B):
+    """Full 32768-score paged rows at the decode batch sizes of the latency
+    sweep, up to twice the compute-unit count."""
+    rng = np.random.Generator(np.random.PCG64(900 + B))
+    L, k, ps = 32768, 1024, 64
+    x = workloads.normal_dense(rng, B, L)
+    pt = np.stack([rng.permutation(L // ps) for _ in range(B)]).astype(np.int32)
+    w = Workload("decode", "paged", k, B, x, L=L, lens=np.full(B, L, dtype=np.int32),
+                 page_table=pt, page_size=ps)
+    print("case decode B", B, flush=True)
+    assert_parity(w, run_gpu(w), run_oracle(w))
