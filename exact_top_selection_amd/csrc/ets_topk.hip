@@ -39,7 +39,13 @@ namespace ets {
 
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
-constexpr int kSmallCap = 128;  // largest bucket ranked by direct comparison
+constexpr int kSmallCap = 128;  // bucket ranked by direct comparison, 8 lanes per entry (1024 lanes)
+// A one-workgroup row ranks buckets of up to kRankCap entries directly, with
+// half as many lanes per entry above kSmallCap: one more radix round on a
+// resident row costs a pass over every slot, a histogram search and the later
+// rounds' histogram copies (up to 5.7 us, measured on rows whose first round
+// left 129 to 256 entries), the wider ranking about 0.5 us.
+constexpr int kRankCap = 256;
 constexpr int kPtCap = 2048;    // page-table entries staged in LDS
 constexpr uint32_t kPeelShare = 16;  // lanes of a wave in one bin that switch to merged atomics
 // Radix rounds needed at most: 12 + 12 + 8 key bits, then 12 + 12 + 7 position
@@ -472,7 +478,7 @@ __device__ __forceinline__ void hist_clear(uint32_t* hist) {
   }
 }
 
-// Radix rounds until the bucket holds at most kSmallCap entries: 12-bit
+// Radix rounds until the bucket holds at most CAP entries: 12-bit
 // rounds on the key inside [lo, hi], then (one key left with too many ties)
 // rounds on d = n - 1 - pos among the scores equal to it, so that the
 // lowest positions win.  Padding slots have pos >= n: their d wraps far
@@ -484,7 +490,7 @@ __device__ __forceinline__ void hist_clear(uint32_t* hist) {
 // caller to resolve by position.  above_free: no key that for_each visits
 // lies above in.hi (otherwise keys above the range go to the dummy bins by a
 // range test in every round).  Returns the refined state.
-template <int T, class ForEach>
+template <int T, int CAP = kSmallCap, class ForEach>
 __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel in, uint32_t nm1,
                                       uint32_t n_pad, uint32_t probe_key, int& round,
                                       bool tie_rounds = true, bool above_free = true,
@@ -493,7 +499,7 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
   uint32_t tie = 0, dlo = 0, dhi = nm1;
   const int first_round = round;
   bool sub_clear = false;  // the copies are zero (cleared before their first use)
-  while (bucket > static_cast<uint32_t>(kSmallCap) && lo != hi && round < kMaxRounds) {
+  while (bucket > static_cast<uint32_t>(CAP) && lo != hi && round < kMaxRounds) {
     uint32_t* hist = sm.hist[round & 1];
     hist_clear<T>(sm.hist[(round + 1) & 1]);
     if (sub != nullptr && round > 0 && !sub_clear) {
@@ -563,10 +569,10 @@ __device__ __forceinline__ Sel refine(ForEach&& for_each, SelSmem& sm, const Sel
     if (hi - lo > width) hi = lo + width;
     ++round;
   }
-  if (bucket > static_cast<uint32_t>(kSmallCap)) {
+  if (bucket > static_cast<uint32_t>(CAP)) {
     tie = 1;
     const uint32_t tkey = lo;
-    while (tie_rounds && bucket > static_cast<uint32_t>(kSmallCap) && round < kMaxRounds) {
+    while (tie_rounds && bucket > static_cast<uint32_t>(CAP) && round < kMaxRounds) {
       uint32_t* hist = sm.hist[round & 1];
       hist_clear<T>(sm.hist[(round + 1) & 1]);
       const uint32_t rdlo = dlo, span = dhi - dlo;
@@ -649,17 +655,17 @@ __device__ __forceinline__ uint64_t bucket_entry(uint32_t key, int32_t pos) {
   return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(pos));
 }
 
-// Ranks up to kSmallCap bucket entries on (key desc, position asc) and emits
-// the kk best at slots first + rank.  G = T / kSmallCap lanes share an entry:
+// Ranks up to CAP bucket entries on (key desc, position asc) and emits
+// the kk best at slots first + rank.  G = T / CAP lanes share an entry:
 // each compares it with every G-th entry, then row permutes sum the G counts.
-// cand holds the nc entries followed by zero words up to kSmallCap, so no
+// cand holds the nc entries followed by zero words up to CAP, so no
 // read is clamped and no comparison tests an index.
-template <int T, class Emit>
+template <int T, int CAP = kSmallCap, class Emit>
 __device__ __forceinline__ void rank_bucket(const uint64_t* cand, uint32_t nc, uint32_t kk,
                                             uint32_t first, Emit&& emit) {
-  constexpr int G = T / kSmallCap;
+  constexpr int G = T / CAP;
   static_assert(G == 2 || G == 4 || G == 8, "2, 4 or 8 lanes per bucket entry");
-  constexpr int Q = kSmallCap / G;  // entries compared by each lane
+  constexpr int Q = CAP / G;  // entries compared by each lane
   constexpr int QB = 4;             // entries read per batch: small buckets read little
   static_assert(Q % QB == 0, "whole batches");
   const uint32_t i = threadIdx.x / G;
@@ -870,7 +876,7 @@ struct alignas(16) RowSmem {
   SelSmem sel;
   uint32_t sub[NSUB > 0 ? NSUB : 1][NSUB > 0 ? kSubStride : 1];  // a later round's histogram copies
   int32_t pt[kPtCap];     // staged page-table row (paged map)
-  uint64_t cand[kSmallCap];  // threshold bucket (bucket_entry words, zero past the bucket)
+  uint64_t cand[kRankCap];  // threshold bucket (bucket_entry words, zero past the bucket)
   int32_t pos[ETS_MAX_K]; // selected positions by output slot
   uint32_t red[64];       // per-wave partials (bounds)
   uint32_t ccount;
@@ -929,7 +935,7 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kS
 
   hist_clear<T>(sm.sel.hist[0]);
   if (tid == 0) sm.ccount = 0;
-  if (tid < kSmallCap) sm.cand[tid] = 0ull;
+  for (int i = tid; i < kRankCap; i += T) sm.cand[i] = 0ull;
   if constexpr (MODE == kPaged) {
     if (pt_lds) {
 #pragma unroll
@@ -948,7 +954,7 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kS
     if (early) {
       sel = early_round<T, VEC>(span, key, sm.sel, sm.red, k, n);
       round = 1;
-      sel = refine<T>(for_each, sm.sel, sel, nm1, span.pad_slots(), key[0], round, !kPrefixTies, false,
+      sel = refine<T, kRankCap>(for_each, sm.sel, sel, nm1, span.pad_slots(), key[0], round, !kPrefixTies, false,
                       T >= 1024 ? &sm.sub[0][0] : nullptr);
     }
   }
@@ -1011,10 +1017,10 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kS
   sel0.bucket = 0xFFFFFFFFu;
 
   // ---- radix refinement until the bucket is small
-  sel = refine<T>(for_each, sm.sel, sel0, nm1, span.pad_slots(), key[0], round, !kPrefixTies, true,
+  sel = refine<T, kRankCap>(for_each, sm.sel, sel0, nm1, span.pad_slots(), key[0], round, !kPrefixTies, true,
                   T >= 1024 ? &sm.sub[0][0] : nullptr);
   }
-  const bool prefix_ties = kPrefixTies && sel.tie && sel.bucket > static_cast<uint32_t>(kSmallCap);
+  const bool prefix_ties = kPrefixTies && sel.tie && sel.bucket > static_cast<uint32_t>(kRankCap);
 
   // ---- scatter: append the bucket to LDS, count the winners, place them by
   // one block scan (whose barrier also publishes the bucket) into the
@@ -1037,14 +1043,14 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kS
   };
   auto append = [&](uint32_t x, int32_t pos) {
     const uint32_t slot = atomicAdd(&sm.ccount, 1u);
-    if (slot < static_cast<uint32_t>(kSmallCap)) sm.cand[slot] = bucket_entry(x, pos);
+    if (slot < static_cast<uint32_t>(kRankCap)) sm.cand[slot] = bucket_entry(x, pos);
   };
   if constexpr (!STREAM) {
     // bit PT-1-j of wmask / cmask: slot j is a winner / in the bucket
     static_assert(PT <= 32, "slot masks are 32 bits");
     uint32_t wmask = 0, cmask = 0;
     if (prefix_ties) {
-      // One key T with more than kSmallCap copies: its sel.kk copies at the
+      // One key T with more than kRankCap copies: its sel.kk copies at the
       // lowest positions win.  Positions grow with (group v of four slots,
       // lane, slot c in the group).  Block totals per group name the group
       // v* that holds the kk-th copy; one block scan of that group's counts
@@ -1157,8 +1163,15 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kS
   }
 
   // ---- the bucket's best kk, placed by rank
-  rank_bucket<T>(sm.cand, min(sm.ccount, static_cast<uint32_t>(kSmallCap)), sel.kk, first,
-                 [&](uint32_t slot, int32_t pos) { sm.pos[slot] = pos; });
+  {
+    const uint32_t nc = min(sm.ccount, static_cast<uint32_t>(kRankCap));
+    auto place = [&](uint32_t slot, int32_t pos) { sm.pos[slot] = pos; };
+    if (nc <= static_cast<uint32_t>(kSmallCap)) {
+      rank_bucket<T>(sm.cand, nc, sel.kk, first, place);
+    } else {
+      rank_bucket<T, kRankCap>(sm.cand, nc, sel.kk, first, place);
+    }
+  }
   __syncthreads();
 
   // ---- emit the k selected positions through the output map, coalesced

@@ -145,13 +145,14 @@ def test_ties_at_the_lowest_key():
         assert_parity(w, run_gpu(w), run_oracle(w))
 
 
-@pytest.mark.parametrize("copies", [1, 2, 64, 127, 128, 129, 200])
+@pytest.mark.parametrize("copies", [1, 2, 64, 127, 128, 129, 200, 255, 256, 257, 300])
 def test_threshold_key_with_copies(copies):
     """The k-th largest score repeated `copies` times at random positions, with
     k - copies // 2 larger scores: the kernel takes the lowest-position half of
-    the copies.  Copies of at most 128 are ranked directly (entries ordered by
-    key, then position); more go through the tie rounds.  Rows that fit one
-    workgroup and rows split over a row group."""
+    the copies.  On one workgroup, copies of at most 256 are ranked directly
+    (entries ordered by key, then position; 8 lanes per entry up to 128, 4
+    above), more are resolved by position; row groups rank at most 128.
+    Rows that fit one workgroup and rows split over a row group."""
     rng = np.random.default_rng(1000 + copies)
     for L, lens in ((32768, [32768, 20000, 8192]), (70001, [70001, 40000])):
         B = len(lens)
