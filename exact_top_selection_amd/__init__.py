@@ -66,6 +66,8 @@ def _load():
             lib.ets_topk_ragged.argtypes = [vp, vp, vp, i32, i64, i32, vp, i64, vp, sz, vp]
             lib.ets_topk_paged_noalloc.argtypes = [vp, i64, i32, i32, vp, vp, i64, i32, i32, vp,
                                                    i64, vp, vp]
+            lib.ets_topk_paged_window.argtypes = [vp, i64, i32, i32, vp, vp, vp, i64, i32, i32, vp,
+                                                  i64, vp, sz, vp]
             lib.ets_workspace_size.argtypes = [i32, i64, i32, i32, ctypes.POINTER(sz)]
             lib.ets_row_split.argtypes = [i32, i64, i32, i32]
             lib.ets_workspace_init.argtypes = [vp, sz, vp]
@@ -77,7 +79,7 @@ def _load():
             lib.ets_floor_read.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp, i64, vp]
             lib.ets_floor_launch.argtypes = [i32, i64, vp]
             for fn in (lib.ets_topk_raw, lib.ets_topk_paged, lib.ets_topk_ragged,
-                       lib.ets_topk_paged_noalloc,
+                       lib.ets_topk_paged_noalloc, lib.ets_topk_paged_window,
                        lib.ets_workspace_size, lib.ets_row_split, lib.ets_workspace_init,
                        lib.ets_workspace_error, lib.ets_device_limits, lib.ets_group_cap,
                        lib.ets_floor_read, lib.ets_floor_launch):
@@ -280,11 +282,14 @@ def topk_raw(scores: torch.Tensor, k: int, lens: Optional[torch.Tensor] = None,
 
 def topk_paged(scores: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.Tensor,
                page_indices: torch.Tensor, page_size: int,
-               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+               workspace: Optional[torch.Tensor] = None,
+               window_starts: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Fills ``page_indices`` int32 [B, k] with the paged slots of each row's top-k.
 
     Slot of position i of row b: page_table[b, i // page_size] * page_size +
-    i % page_size.  ``k`` is ``page_indices.shape[1]``.
+    i % page_size.  ``k`` is ``page_indices.shape[1]``.  With ``window_starts``
+    (int32 [B]) row b selects among positions [window_starts[b], seq_lens[b])
+    only (ets_topk_paged_window).
     """
     _require(scores, "scores", torch.float32, 2)
     B, L = scores.shape
@@ -304,15 +309,28 @@ def topk_paged(scores: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.T
     if page_table.shape[1] * page_size < L:
         raise ValueError("page_table has %d pages of %d, fewer than L = %d positions"
                          % (page_table.shape[1], page_size, L))
+    if window_starts is not None:
+        _vec(window_starts, "window_starts", B)
+        if window_starts.device != dev:
+            raise ValueError("window_starts must be on %s" % dev)
     ws, ws_bytes = _workspace(B, L, k, dev, workspace)
     with torch.cuda.device(dev):
-        st = _load().ets_topk_paged(scores.data_ptr(), _rows(scores, "scores"), B, L,
-                                    seq_lens.data_ptr(), page_table.data_ptr(),
-                                    _rows(page_table, "page_table"), page_size, k,
-                                    out.data_ptr(), out.stride(0) if B > 1 else k,
-                                    ws.data_ptr() if ws is not None else None, ws_bytes,
-                                    _stream(dev))
-    _check(st, "ets_topk_paged")
+        if window_starts is None:
+            st = _load().ets_topk_paged(scores.data_ptr(), _rows(scores, "scores"), B, L,
+                                        seq_lens.data_ptr(), page_table.data_ptr(),
+                                        _rows(page_table, "page_table"), page_size, k,
+                                        out.data_ptr(), out.stride(0) if B > 1 else k,
+                                        ws.data_ptr() if ws is not None else None, ws_bytes,
+                                        _stream(dev))
+        else:
+            st = _load().ets_topk_paged_window(scores.data_ptr(), _rows(scores, "scores"), B, L,
+                                               window_starts.data_ptr(), seq_lens.data_ptr(),
+                                               page_table.data_ptr(),
+                                               _rows(page_table, "page_table"), page_size, k,
+                                               out.data_ptr(), out.stride(0) if B > 1 else k,
+                                               ws.data_ptr() if ws is not None else None,
+                                               ws_bytes, _stream(dev))
+    _check(st, "ets_topk_paged" if window_starts is None else "ets_topk_paged_window")
     return out
 
 

@@ -73,6 +73,7 @@ struct Params {
   int64_t row_stride;          // dense rows
   const int32_t* lens;         // dense valid lengths (nullable) or ragged lengths
   const int32_t* row_starts;   // ragged
+  const int32_t* win_starts;   // dense windows (nullable): row b selects among [win_starts[b], n_b)
   const int32_t* page_table;   // paged
   int64_t pt_stride;
   int32_t page_size;
@@ -625,26 +626,28 @@ __device__ __forceinline__ bool sel_bucket(const Sel& s, uint32_t nm1, int32_t e
 using lds_i32 = __attribute__((address_space(3))) const int32_t;
 using glb_i32 = __attribute__((address_space(1))) const int32_t;
 
-// Output value of selected position pos of a row.  Paged: pt_lds is the
-// row's page-table staged in LDS, used when use_lds, else pt_row is read.
+// Output value of selected position pos of a row: pos counts from the row's
+// first candidate, row_start is that candidate's position (dense rows: the
+// window start, 0 without windows; ragged rows: the row's offset in the
+// packed buffer).  Paged: pt_lds is the row's page-table staged in LDS, used
+// when use_lds, else pt_row is read.
 template <int MODE>
 __device__ __forceinline__ int32_t out_value(const Params& p, bool use_lds, const int32_t* pt_lds,
                                              const int32_t* pt_row, int32_t row_start, int32_t pos) {
   if constexpr (MODE == kPaged) {
+    const int32_t a = row_start + pos;  // position in the row
     int32_t page, off;
     if (p.page_shift >= 0) {
-      page = pos >> p.page_shift;
-      off = pos & (p.page_size - 1);
+      page = a >> p.page_shift;
+      off = a & (p.page_size - 1);
     } else {
-      page = pos / p.page_size;
-      off = pos - page * p.page_size;
+      page = a / p.page_size;
+      off = a - page * p.page_size;
     }
     const int32_t id = use_lds ? ((lds_i32*)pt_lds)[page] : ((glb_i32*)pt_row)[page];
     return id * p.page_size + off;
-  } else if constexpr (MODE == kRagged) {
-    return row_start + pos;
   } else {
-    return pos;
+    return row_start + pos;
   }
 }
 
@@ -689,7 +692,10 @@ __device__ __forceinline__ void rank_bucket(const uint64_t* cand, uint32_t nc, u
   if (i < nc && part == 0 && rank < kk) emit(first + rank, static_cast<int32_t>(~static_cast<uint32_t>(vi)));
 }
 
-// Row geometry shared by every kernel: valid length, base pointer, offsets.
+// Row geometry shared by every kernel: the candidates of row b are the n
+// scores from `row` on; row_start is the position of the first of them (see
+// out_value).  Dense rows: n_b = their length clamped to [0, L]; with windows,
+// the candidates start at the window start clamped to [0, n_b].
 template <int MODE>
 struct RowRef {
   int32_t n;
@@ -704,8 +710,10 @@ struct RowRef {
       n = max(p.lens[b], 0);
       row = p.scores + row_start;
     } else {
-      n = p.lens ? min(max(p.lens[b], 0), p.L) : p.L;
-      row = p.scores + static_cast<int64_t>(b) * p.row_stride;
+      const int32_t nb = p.lens ? min(max(p.lens[b], 0), p.L) : p.L;
+      row_start = p.win_starts ? min(max(p.win_starts[b], 0), nb) : 0;
+      n = nb - row_start;
+      row = p.scores + static_cast<int64_t>(b) * p.row_stride + row_start;
     }
     pt_row = (MODE == kPaged) ? p.page_table + static_cast<int64_t>(b) * p.pt_stride : nullptr;
     out = p.out + static_cast<int64_t>(b) * p.out_stride;
@@ -903,7 +911,9 @@ __device__ __forceinline__ void row_topk(const Params& p, RowSmem<T >= 1024 ? kS
   bool pt_lds = false;
   int32_t npages = 0;
   if constexpr (MODE == kPaged) {
-    npages = p.page_shift >= 0 ? ((n - 1) >> p.page_shift) + 1 : (n - 1) / p.page_size + 1;
+    // pages of positions [0, row_start + n): with a window, those before it too
+    const int32_t last = r.row_start + n - 1;
+    npages = p.page_shift >= 0 ? (last >> p.page_shift) + 1 : last / p.page_size + 1;
     pt_lds = npages <= kPtCap;
     if (pt_lds) {
 #pragma unroll
@@ -1536,8 +1546,8 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   bool pt_lds = false;
   if constexpr (MODE == kPaged) {
     if (p.page_shift >= 0 && span.end > span.start) {
-      p0 = span.start >> p.page_shift;
-      np = ((span.end - 1) >> p.page_shift) - p0 + 1;
+      p0 = (r.row_start + span.start) >> p.page_shift;
+      np = ((r.row_start + span.end - 1) >> p.page_shift) - p0 + 1;
       pt_lds = np <= kGroupPtCap;
       if (pt_lds) {
 #pragma unroll
@@ -1818,7 +1828,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     for (uint32_t i = tid; i < wtot; i += T) {
       const uint32_t slot = wbase + i;
       if (slot < first && i < static_cast<uint32_t>(ETS_MAX_K)) {
-        const int32_t pos = sm.u.pos[i];
+        const int32_t pos = r.row_start + sm.u.pos[i];  // position in the row
         r.out[slot] = ((lds_i32*)sm.pt)[(pos >> sh) - p0] * ps + (pos & (ps - 1));
       }
     }
@@ -2505,6 +2515,41 @@ ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, in
   auto s = static_cast<hipStream_t>(stream);
   return v4 ? launch<ets::kPaged, true>(p, B, L, info, workspace, s)
             : launch<ets::kPaged, false>(p, B, L, info, workspace, s);
+}
+
+ets_status ets_topk_paged_window(const float* scores, int64_t row_stride, int32_t B, int32_t L,
+                                 const int32_t* window_starts, const int32_t* seq_lens,
+                                 const int32_t* page_table, int64_t pt_stride, int32_t page_size,
+                                 int32_t k, int32_t* out, int64_t out_stride, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (window_starts == nullptr)
+    return ets_topk_paged(scores, row_stride, B, L, seq_lens, page_table, pt_stride, page_size, k, out,
+                          out_stride, workspace, workspace_bytes, stream);
+  if (k < 1 || k > ETS_MAX_K) return ETS_ERR_K_RANGE;
+  if (B < 0 || L < 0 || row_stride < L || out_stride < k || page_size < 1 || pt_stride < 0)
+    return ETS_ERR_INVALID_ARG;
+  if (B == 0) return ETS_OK;
+  if (!out || !seq_lens || !page_table || (L > 0 && !scores)) return ETS_ERR_INVALID_ARG;
+  int dev;
+  DeviceInfo info;
+  if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
+  if (ets_status st = check_workspace(B, L, info, workspace, workspace_bytes); st != ETS_OK)
+    return st;
+  ets::Params p{};
+  p.scores = scores;
+  p.row_stride = row_stride;
+  p.lens = seq_lens;
+  p.win_starts = window_starts;
+  p.page_table = page_table;
+  p.pt_stride = pt_stride;
+  p.page_size = page_size;
+  p.page_shift = page_shift_of(page_size);
+  p.L = L;
+  p.k = k;
+  p.out = out;
+  p.out_stride = out_stride;
+  // a window start moves a row's first score off the 16-byte grid: dword loads
+  return launch<ets::kPaged, false>(p, B, L, info, workspace, static_cast<hipStream_t>(stream));
 }
 
 ets_status ets_topk_paged_noalloc(const float* scores, int64_t row_stride, int32_t B, int32_t L,

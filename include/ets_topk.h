@@ -112,6 +112,27 @@ ets_status ets_topk_paged(const float* scores, int64_t row_stride, int32_t B, in
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Dense rows with a window per row, paged output: the decode caller's map
+ * when only the last part of each sequence is a candidate (a sliding
+ * window).  The pages' row-start offsets (PR #37591 digest, the CoopParams
+ * excerpt; its tests cover "variable windows" on all three entry points)
+ * address packed ragged rows; this call gives a dense row the same start.
+ *   window_starts int32 [B]: row b selects among positions
+ *              [w_b, n_b), n_b = seq_lens[b] clamped to [0, L] and w_b =
+ *              window_starts[b] clamped to [0, n_b]; NULL = ets_topk_paged.
+ *   Every other argument, the result, the padding and the workspace are as
+ *   for ets_topk_paged; selected positions are row positions (i >= w_b), so
+ *   out holds page_table[b][i / page_size] * page_size + i % page_size.
+ *   A window start is not 16-byte aligned in general, so these rows are read
+ *   with 4-byte loads.
+ */
+ets_status ets_topk_paged_window(const float* scores, int64_t row_stride, int32_t B, int32_t L,
+                                 const int32_t* window_starts, const int32_t* seq_lens,
+                                 const int32_t* page_table, int64_t pt_stride, int32_t page_size,
+                                 int32_t k, int32_t* out, int64_t out_stride, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the paged
  * call above with the same arguments and results, but with no workspace

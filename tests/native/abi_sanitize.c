@@ -44,6 +44,10 @@ int main(void) {
   EXPECT(ets_topk_paged(fs, 64, 1, 64, NULL, fi, 1, 64, 8, fi, 8, NULL, 0, NULL), ETS_ERR_INVALID_ARG);
   EXPECT(ets_topk_paged(fs, 64, 1, 64, fi, NULL, 1, 64, 8, fi, 8, NULL, 0, NULL), ETS_ERR_INVALID_ARG);
   EXPECT(ets_topk_paged(fs, 64, 1, 64, fi, fi, -1, 64, 8, fi, 8, NULL, 0, NULL), ETS_ERR_INVALID_ARG);
+  EXPECT(ets_topk_paged_window(fs, 64, 1, 64, fi, fi, fi, 1, 0, 8, fi, 8, NULL, 0, NULL), ETS_ERR_INVALID_ARG);
+  EXPECT(ets_topk_paged_window(fs, 64, 1, 64, fi, NULL, fi, 1, 64, 8, fi, 8, NULL, 0, NULL), ETS_ERR_INVALID_ARG);
+  EXPECT(ets_topk_paged_window(fs, 64, 1, 64, fi, fi, fi, 1, 64, 4096, fi, 4096, NULL, 0, NULL), ETS_ERR_K_RANGE);
+  EXPECT(ets_topk_paged_window(NULL, 0, 0, 0, fi, NULL, NULL, 0, 64, 8, NULL, 8, NULL, 0, NULL), ETS_OK);
   EXPECT(ets_topk_paged_noalloc(fs, 64, 1, 64, fi, fi, 1, 64, 0, fi, 8, NULL, NULL), ETS_ERR_K_RANGE);
   EXPECT(ets_topk_paged_noalloc(fs, 64, 1, 64, fi, fi, 1, 0, 8, fi, 8, NULL, NULL), ETS_ERR_INVALID_ARG);
   EXPECT(ets_topk_paged_noalloc(fs, 64, 1, 64, NULL, fi, 1, 64, 8, fi, 8, NULL, NULL), ETS_ERR_INVALID_ARG);

@@ -477,3 +477,73 @@ def test_decode_batches(B):
                  page_table=pt, page_size=ps)
     print("case decode B", B, flush=True)
     assert_parity(w, run_gpu(w), run_oracle(w))
+
+
+def _window_oracle(x, lens, wins, pt, ps, k):
+    """Each row's window [w_b, n_b) selected by the oracle's ragged call on the
+    rows' flat buffer (row b's window starts at b * L + w_b), then mapped to
+    paged slots of the row positions."""
+    import oracle
+    B, L = x.shape
+    n = np.clip(lens.astype(np.int64), 0, L)
+    w = np.clip(wins.astype(np.int64), 0, n)
+    starts = (np.arange(B) * L + w).astype(np.int32)
+    flat = oracle.topk_ragged(np.ascontiguousarray(x.reshape(-1)), starts, (n - w).astype(np.int32), k)
+    out = np.full((B, k), -1, np.int32)
+    for b in range(B):
+        v = flat[b][flat[b] != -1].astype(np.int64) - b * L
+        out[b, :v.size] = pt[b, v // ps] * ps + v % ps
+    return out
+
+
+def _run_window(x, lens, wins, pt, ps, k):
+    d = dev()
+    out = torch.full((x.shape[0], k), POISON, dtype=torch.int32, device=d)
+    ets.topk_paged(torch.from_numpy(x).to(d), torch.from_numpy(lens).to(d),
+                   torch.from_numpy(pt).to(d), out, ps, window_starts=torch.from_numpy(wins).to(d))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("ps", [64, 48])
+@pytest.mark.parametrize("L", [32768, 70000])
+def test_paged_windows(L, ps):
+    """A window per row on the paged call (ets_topk_paged_window): row b selects
+    among [window_starts[b], seq_lens[b]), both clamped, and emits paged slots
+    of row positions; rows that fit one workgroup (L = 32768) and rows split
+    over row groups (L = 70000)."""
+    rng = np.random.default_rng(3000 + L + ps)
+    lens = np.array([L, L, L - 7, 20001, 5000, 2049, 1500, L, L], dtype=np.int32)
+    wins = np.array([0, 1, 63, 64 * 7, 1000, 2048, 2000, L - 1, -3], dtype=np.int32)
+    B = lens.size
+    x = rng.standard_normal((B, L)).astype(np.float32)
+    npg = -(-L // ps)
+    pt = np.stack([rng.permutation(npg) for _ in range(B)]).astype(np.int32)
+    for k in (1, 1024, 2048):
+        print("case windows L", L, "ps", ps, "k", k, flush=True)
+        got = _run_window(x, lens, wins, pt, ps, k)
+        want = _window_oracle(x, lens, wins, pt, ps, k)
+        gs, ws_ = np.sort(got, axis=1), np.sort(want, axis=1)
+        bad = np.nonzero((gs != ws_).any(axis=1))[0]
+        assert bad.size == 0, "rows %s differ" % bad.tolist()
+
+
+def test_paged_windows_on_page_boundaries():
+    """Windows that start on a page boundary equal the plain paged call on the
+    rows shifted by the window, with the page table shifted by its pages: the
+    oracle's own paged map, no formula in the test."""
+    import oracle
+    rng = np.random.default_rng(3100)
+    B, L, ps, k = 5, 32768, 64, 1024
+    lens = np.array([L, 30000, 12345, 4096, L], dtype=np.int32)
+    wins = np.array([0, 64, 640, 4096, 64 * 500], dtype=np.int32)
+    x = rng.standard_normal((B, L)).astype(np.float32)
+    pt = np.stack([rng.permutation(L // ps) for _ in range(B)]).astype(np.int32)
+    got = _run_window(x, lens, wins, pt, ps, k)
+    xs = np.zeros_like(x)
+    pts = np.zeros_like(pt)
+    for b in range(B):
+        xs[b, :L - wins[b]] = x[b, wins[b]:]
+        pts[b, :pt.shape[1] - wins[b] // ps] = pt[b, wins[b] // ps:]
+    want = oracle.topk_paged(xs, (lens - wins).astype(np.int32), pts, ps, k)
+    np.testing.assert_array_equal(np.sort(got, axis=1), np.sort(want, axis=1))
