@@ -703,7 +703,7 @@ struct RowRef {
   const float* row;
   const int32_t* pt_row;
   int32_t* out;
-  __device__ RowRef(const Params& p, int b) {
+  __device__ __forceinline__ RowRef(const Params& p, int b) {
     row_start = 0;
     if constexpr (MODE == kRagged) {
       row_start = p.row_starts[b];

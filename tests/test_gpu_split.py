@@ -204,6 +204,62 @@ def test_ragged_row_longer_than_hint():
         assert_parity(w, out.cpu().numpy(), run_oracle(w))
 
 
+def _edge_rows(rng, lengths, first_lead, kinds):
+    """A packed buffer of ragged rows: row b starts (first_lead + b) % 4
+    scores past a 16-byte boundary, rows are separated by 4 to 7 scores of
+    +1e30 that belong to no row (larger than any row score: a neighbour's
+    score read as the row's would be selected), and the last row ends the
+    buffer 1 to 3 scores past a 16-byte boundary (one score shorter than
+    asked where it would end on one).  kinds[b]: "normal" N(0,1); "pad-key" mostly the bit pattern
+    0xFFFFFFFF (key 0, the padding's key) with fewer other scores than k
+    asks, so the threshold is key 0 and ties go by position; "equal" all 1.0."""
+    parts, starts, lens = [], [], []
+    pos = 0
+    for b, n in enumerate(lengths):
+        lead = (first_lead + b) % 4
+        gap = (lead - pos) % 4 + (4 if b else 0)
+        if b == len(lengths) - 1 and (pos + gap + n) % 4 == 0:
+            n -= 1
+        parts.append(np.full(gap, 1e30, dtype=np.float32))
+        pos += gap
+        starts.append(pos)
+        lens.append(n)
+        if kinds[b] == "normal":
+            row = rng.standard_normal(n).astype(np.float32)
+        elif kinds[b] == "equal":
+            row = np.ones(n, dtype=np.float32)
+        else:
+            row = np.full(n, 0xFFFFFFFF, dtype=np.uint32).view(np.float32)
+            few = rng.choice(n, size=min(n, 40), replace=False)
+            row[few] = rng.standard_normal(few.size).astype(np.float32)
+        parts.append(row)
+        pos += n
+    packed = np.ascontiguousarray(np.concatenate(parts))
+    return packed, np.array(starts, dtype=np.int32), np.array(lens, dtype=np.int32)
+
+
+@pytest.mark.parametrize("first_lead", [0, 1, 2, 3])
+def test_ragged_row_edges(first_lead):
+    """Packed ragged rows on the row-group path, starting at every offset
+    from a 16-byte boundary: nothing outside a row is ever selected, whatever
+    its neighbours hold, also where the threshold is the padding slots' own
+    key (0) and ties go by position."""
+    rng = np.random.default_rng(500 + first_lead)
+    lengths = [5003, 4098, 7001, 3073, 6150]
+    kinds = ["normal", "pad-key", "equal", "pad-key", "normal"]
+    packed, starts, lens = _edge_rows(rng, lengths, first_lead, kinds)
+    assert ((starts % 4) == (first_lead + np.arange(5)) % 4).all()
+    assert starts[-1] + lens[-1] == packed.size and packed.size % 4 != 0
+    d = dev()
+    for k in (64, 1000, 2048):
+        w = Workload("ragged-edges", "ragged", k, 5, packed, row_starts=starts, lengths=lens)
+        want = run_oracle(w)
+        for g in (2, 3, 8):
+            with split(g):
+                print("first_lead", first_lead, "k", k, "G", g, flush=True)
+                assert_parity(w, run_gpu(w), want)
+
+
 def test_one_workspace_across_shapes_and_apis():
     """Every call returns its workspace's counters and tables to zero, so one
     buffer serves calls of any shape and map in turn."""
