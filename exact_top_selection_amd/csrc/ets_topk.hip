@@ -1902,27 +1902,39 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   }
 }
 
-// One launch for the whole batch: B * G workgroups, G per row.  TICKET:
+// One launch for the whole batch, G workgroups per row.  TICKET: B * G
 // workgroups take rows in the order they start (a device counter), so that
 // a group only waits for members that have started or start next and
 // progress needs room for one group on one XCD (G at most one XCD's
-// row-group slots, checked by the host).  Otherwise workgroup i is member
-// i % G of row i / G; the host chooses this only when the whole grid fits
-// the device's row-group slots at once, where waiting members can never keep
-// the rest of the grid from starting (work of other streams that holds
-// compute units only delays them, until it ends).
+// row-group slots, checked by the host).  Otherwise members are assigned by
+// workgroup index: the dispatcher deals workgroup i to XCD i % nx, and the
+// grid (nx * G * ceil(B / nx) workgroups, the padding idle) gives each row
+// the G workgroups of one XCD, so that its exchanges wait only for that
+// XCD's starts (XCDs start a launch up to 2 us apart; on MI355X, C5 13.4 us
+// against 14.1 with rows spread over every XCD).  The placement only affects
+// speed.  The host chooses this only when the whole grid fits the device's
+// row-group slots at once, where waiting members can never keep the rest of
+// the grid from starting, wherever they run (work of other streams that
+// holds compute units only delays them, until it ends).
 template <int T, int VEC, int MODE, bool V4, bool TICKET>
-__global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, int32_t B, int32_t G) {
+__global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, int32_t B, int32_t G,
+                                                       int32_t nx) {
   __shared__ GroupSmem sm;
   const GroupWs w(ws);
-  uint32_t ticket = blockIdx.x;
+  int b, g;
   if constexpr (TICKET) {
     if (threadIdx.x == 0) sm.ticket = add_dev(w.hdr + kHdrTicket, 1u);
     __syncthreads();
-    ticket = sm.ticket;
+    b = static_cast<int>(sm.ticket / static_cast<uint32_t>(G));
+    g = static_cast<int>(sm.ticket % static_cast<uint32_t>(G));
+  } else {
+    // workgroup i starts on XCD i % nx: row b's members are the workgroups
+    // of XCD b % nx, so that a row's exchanges wait for one XCD's starts only
+    const uint32_t x = blockIdx.x % static_cast<uint32_t>(nx), s = blockIdx.x / static_cast<uint32_t>(nx);
+    b = static_cast<int>(x + static_cast<uint32_t>(nx) * (s / static_cast<uint32_t>(G)));
+    g = static_cast<int>(s % static_cast<uint32_t>(G));
+    if (b >= B) return;  // the grid's padding
   }
-  const int b = static_cast<int>(ticket / static_cast<uint32_t>(G));
-  const int g = static_cast<int>(ticket % static_cast<uint32_t>(G));
   if (b >= B) {
     // only a workspace that was not zero (a stale ticket) gets here: this
     // workgroup's chunk goes unselected, so the call's output is undefined
@@ -2206,20 +2218,25 @@ void launch_rows(const ets::Params& p, int32_t B, hipStream_t stream) {
                      p);
 }
 
-// Members are assigned by workgroup index only when the whole grid fits the
-// device's row-group slots at once (each compute unit holds group_occ of
-// them); otherwise by ticket in start order (see group_topk_kernel).
+// Members are assigned by workgroup index, one XCD per row, only when the
+// whole padded grid fits the device's row-group slots at once (each compute
+// unit holds group_occ of them); otherwise by ticket in start order (see
+// group_topk_kernel).
 template <int MODE, bool V4, int VEC>
 void launch_group(const ets::Params& p, int32_t B, int32_t G, const DeviceInfo& info, void* ws,
                   hipStream_t stream) {
   const uint32_t grid = static_cast<uint32_t>(B) * static_cast<uint32_t>(G);
   const int64_t slots = static_cast<int64_t>(info.cu_count) * info.group_occ;
-  if (static_cast<int64_t>(grid) <= slots) {
-    hipLaunchKernelGGL((ets::group_topk_kernel<kGroupThreads, VEC, MODE, V4, false>), dim3(grid),
-                       dim3(kGroupThreads), 0, stream, p, static_cast<uint32_t*>(ws), B, G);
+  const int32_t nx = std::max(info.xcd_count, 1);
+  // by index: nx * G workgroups per nx rows, padded to whole rows per XCD
+  const int64_t padded = static_cast<int64_t>(nx) * G * ((B + nx - 1) / nx);
+  if (padded <= slots) {
+    hipLaunchKernelGGL((ets::group_topk_kernel<kGroupThreads, VEC, MODE, V4, false>),
+                       dim3(static_cast<uint32_t>(padded)), dim3(kGroupThreads), 0, stream, p,
+                       static_cast<uint32_t*>(ws), B, G, nx);
   } else {
     hipLaunchKernelGGL((ets::group_topk_kernel<kGroupThreads, VEC, MODE, V4, true>), dim3(grid),
-                       dim3(kGroupThreads), 0, stream, p, static_cast<uint32_t*>(ws), B, G);
+                       dim3(kGroupThreads), 0, stream, p, static_cast<uint32_t*>(ws), B, G, nx);
   }
 }
 
