@@ -1229,8 +1229,8 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 //    slot, one 64-bit store that also marks the slot written; the members
 //    poll the row's G slots and take the largest key and the best bound;
 //  * round 0: every member builds a 12-bit LDS histogram of its chunk over
-//    [lower bound, largest key], merges 16 fine bins to one and adds the
-//    256 coarse bins into the row's table, and the count of its scores
+//    [lower bound, largest key], merges 8 fine bins to one and adds the
+//    512 coarse bins into the row's table, and the count of its scores
 //    under the lower bound into one more word; one wave of every member
 //    polls the table until it and that word hold all n scores of the row
 //    (no barrier: the total reaches n only once every member's adds have
@@ -1244,9 +1244,9 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 //    (LDS radix rounds, then direct comparison), emits the rest of the row
 //    and returns the row's workspace to zero.
 //
-// Workgroup i is member i % G of row i / G when the whole grid fits the
-// device's row-group slots at once; otherwise groups are formed in the order
-// workgroups start (a ticket counter).  Why a ticketed grid always finishes
+// Members are assigned by workgroup index, a row's G members on one XCD,
+// when the whole grid fits the device's row-group slots at once; otherwise
+// groups are formed in the order workgroups start (a ticket counter).  Why a ticketed grid always finishes
 // when G is at most the row-group slots of one XCD (its compute units times
 // the workgroups one compute unit holds; the host derives that cap from the
 // device): tickets are consecutive, so every group whose G tickets are all
@@ -1655,7 +1655,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     if (lo == 0 && tid == 0) lh[0] -= pad;  // padding slots hold key 0
     __syncthreads();
   }
-  // the row's histogram, 16 bins to one: few device atomics per member, and a
+  // the row's histogram, 8 bins to one: few device atomics per member, and a
   // coarse threshold bucket that the tie list absorbs; with it the count of
   // the chunk's scores under lo, so that the table tells when it is whole
   {
