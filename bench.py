@@ -230,11 +230,14 @@ def main() -> int:
                     help="skip the empty-launch and read-only floors")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload lines (C1 .. C5) after the headline")
-    ap.add_argument("--sweep", choices=["batch", "k"],
+    ap.add_argument("--sweep", choices=["batch", "k", "spread"],
                     help="instead of the headline: one JSON line per point of a sweep, "
                          "'batch' = paged decode rows of 32768 scores, k = 1024, B in "
                          "1 .. 512 (HIP graph and eager launches); 'k' = the C3 workload with "
-                         "k in 1 .. 2048")
+                         "k in 1 .. 2048; 'spread' = raw rows of up to 262144 scores, "
+                         "k = 2048, B in 4 .. 64, lengths all L or uniform in [L/2, L] or "
+                         "[L/8, L], the split heuristic's choice against forced "
+                         "workgroups per row (ETS_ROW_SPLIT)")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a HIP graph")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -338,13 +341,60 @@ def main() -> int:
     return 0
 
 
+def sweep_spread(torch, ets, workloads, args, dev, cu, cap, steps) -> int:
+    """The split heuristic sees only the longest row (the lengths stay on the
+    device): rows whose lengths spread below it, timed with the heuristic's
+    choice and with each forced number of workgroups per row."""
+    from workloads import Workload
+    L, k = 262144, 2048
+    forced = (None, 0, 4, 8, 16, 32)
+    old = os.environ.get("ETS_ROW_SPLIT")
+    try:
+        for B in (4, 16, 64):
+            for lo_div in (1, 2, 8):
+                rng = np.random.Generator(np.random.PCG64(args.seed + 1000 * B + lo_div))
+                x = workloads.normal_dense(rng, B, L)
+                lens = (np.full(B, L, dtype=np.int32) if lo_div == 1 else
+                        rng.integers(L // lo_div, L, size=B, endpoint=True).astype(np.int32))
+                spread = "all L" if lo_div == 1 else "U[L/%d, L]" % lo_div
+                for g in forced:
+                    if g is None:
+                        os.environ.pop("ETS_ROW_SPLIT", None)
+                    else:
+                        os.environ["ETS_ROW_SPLIT"] = str(g)
+                    w = Workload("spread-B%d-L%d-%s" % (B, L, spread), "raw", k, B, x, L=L,
+                                 lens=lens, note="raw, N(0,1), lengths " + spread)
+                    rig = Rig(torch, ets, w, dev, cu, cap)
+                    us_g = timed(torch, rig.step, steps, args.warmup, False) * 1e3 / steps
+                    if rig.ws is not None:
+                        assert ets.workspace_error(rig.ws) == 0, "a bounded wait expired"
+                    ab = algorithmic_bytes(w)
+                    print(json.dumps({"point": w.name, "B": B, "L": L, "k": k, "lengths": spread,
+                                      "mean_len": float(lens.mean()),
+                                      "split": "heuristic" if g is None else "forced",
+                                      "groups": rig.split, "us_per_call_graph": us_g,
+                                      "gb_per_s": ab / (us_g * 1e-6) / 1e9, "calls": steps}),
+                          flush=True)
+                    del rig
+                    torch.cuda.empty_cache()
+    finally:
+        if old is None:
+            os.environ.pop("ETS_ROW_SPLIT", None)
+        else:
+            os.environ["ETS_ROW_SPLIT"] = old
+    return 0
+
+
 def sweep(torch, ets, workloads, args) -> int:
-    """Latency against batch size (the decode caller's flat region) or against k."""
+    """Latency against batch size (the decode caller's flat region), against
+    k, or against the spread of row lengths under the split heuristic."""
     from workloads import Workload
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cu, _, cap = ets.device_limits()
     steps = max(args.steps, 200)
+    if args.sweep == "spread":
+        return sweep_spread(torch, ets, workloads, args, dev, cu, cap, steps)
     points = []
     if args.sweep == "batch":
         L, k, ps = 32768, 1024, 64

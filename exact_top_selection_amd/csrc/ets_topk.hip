@@ -82,6 +82,7 @@ struct Params {
   int32_t k;
   int32_t* out;
   int64_t out_stride;
+  int32_t min_chunk;           // row groups: fewest scores in a member's chunk (see member_chunk)
 };
 
 // Order-preserving key: negative -> all bits inverted, else sign bit set
@@ -1286,6 +1287,20 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // the tables to zero (tie lists may keep stale entries).
 
 constexpr int kTieCap = 4096;      // tie-list entries per row
+// Scores per member of a split row: n / G rounded up to a multiple of 4
+// (float4 groups), but at least min_chunk (a multiple of 4; by default
+// kMinChunk), so that a member's lanes hold at least 4096 scores and their
+// two largest keys each give a lower bound of the row's k-th largest
+// (k <= 2048 = 1024 lanes x 2).  A row shorter than G * min_chunk leaves its
+// last members empty.  Measured on MI355X (raw rows, k = 2048, N(0,1),
+// lengths U[32768, 262144], B = 4, G = 16): 23.2 us with chunks of n / G,
+// where the shorter rows get no bound at all and their first round spans
+// the whole key range.
+constexpr int32_t kMinChunk = 4096;
+__host__ __device__ __forceinline__ int64_t member_chunk(int64_t n, int32_t G, int32_t min_chunk) {
+  const int64_t c = ((n + G - 1) / G + 3) & ~static_cast<int64_t>(3);
+  return c > min_chunk ? c : min_chunk;
+}
 // Round 0 exchanges 2^kCoarseBits bins per row.  Measured on MI355X (HIP
 // graph of 300 calls): 512 bins against 256 cut the banded ragged rows of
 // 65536 to 262144 scores (B = 4, k = 2048) from 14.97 to 14.10 us, and N(0,1)
@@ -1945,7 +1960,7 @@ __global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, i
       if (g == 0) emit_whole_row<T, MODE>(p, r);
     } else {
       using SpanT = Span<T, VEC, V4>;
-      const int64_t chunk = ((static_cast<int64_t>(r.n) + G - 1) / G + 3) & ~static_cast<int64_t>(3);
+      const int64_t chunk = member_chunk(r.n, G, p.min_chunk);
       const int32_t start = static_cast<int32_t>(min(static_cast<int64_t>(g) * chunk, static_cast<int64_t>(r.n)));
       const int32_t end = (g == G - 1) ? r.n : static_cast<int32_t>(min(start + chunk, static_cast<int64_t>(r.n)));
       const SpanT span{r.row, start, end};
@@ -1997,7 +2012,7 @@ __global__ __launch_bounds__(T) void floor_read_kernel(Params p, uint32_t* sink,
   const int b = static_cast<int>(blockIdx.x / static_cast<uint32_t>(G));
   const int g = static_cast<int>(blockIdx.x % static_cast<uint32_t>(G));
   const RowRef<MODE> r(p, b);
-  const int64_t chunk = ((static_cast<int64_t>(r.n) + G - 1) / G + 3) & ~static_cast<int64_t>(3);
+  const int64_t chunk = member_chunk(r.n, G, p.min_chunk);
   const int32_t start = static_cast<int32_t>(min(static_cast<int64_t>(g) * chunk, static_cast<int64_t>(r.n)));
   const int32_t end = (g == G - 1) ? r.n : static_cast<int32_t>(min(start + chunk, static_cast<int64_t>(r.n)));
   const SpanT span{r.row, start, end};
@@ -2172,6 +2187,22 @@ int group_kernel_occupancy() {
 // bounds; max_group <= 0 (unknown) leaves the workspace's slot count as the
 // only cap.  ETS_ROW_SPLIT overrides: 0 or 1 = one workgroup per row, n >= 2
 // = n workgroups per row, n <= max_group.
+// Fewest scores per member chunk of a split row: ets::kMinChunk, or the
+// environment variable ETS_MIN_CHUNK (read at every call) when it is an
+// integer >= 1, rounded up to a multiple of 4 and capped at one 32768-score
+// tile.
+int32_t min_chunk_setting() {
+  if (const char* e = std::getenv("ETS_MIN_CHUNK"); e != nullptr && *e != '\0') {
+    char* end = nullptr;
+    const long v = std::strtol(e, &end, 10);
+    if (end != e && *end == '\0' && v >= 1) {
+      const int64_t c = (std::min<int64_t>(v, kRowTile) + 3) & ~static_cast<int64_t>(3);
+      return static_cast<int32_t>(c);
+    }
+  }
+  return ets::kMinChunk;
+}
+
 int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count, int32_t max_group) {
   if (B <= 0 || max_len <= 0) return 0;
   const int64_t cap = max_group > 0 ? std::min<int64_t>(max_group, kGroupSlotCap) : kGroupSlotCap;
@@ -2260,15 +2291,17 @@ Shape launch_shape(int32_t B, int64_t max_len, const DeviceInfo& info) {
     if (max_len <= kRowTile / 2) return {1, kRowThreads, kRowVec / 2, false};
     return {1, kRowThreads, kRowVec, max_len > kRowTile};
   }
-  const int64_t chunk = ((max_len + G - 1) / G + 3) / 4 * 4;
+  const int64_t chunk = ets::member_chunk(max_len, G, min_chunk_setting());
   const int32_t vec = chunk <= kGroupThreads * 4 ? 1 : chunk <= kGroupThreads * 8 ? 2
                     : chunk <= kGroupThreads * 16 ? 4 : 8;
   return {G, kGroupThreads, vec, false};
 }
 
 template <int MODE, bool V4>
-ets_status launch(const ets::Params& p, int32_t B, int64_t max_len, const DeviceInfo& info, void* ws,
-                  hipStream_t stream) {
+ets_status launch(const ets::Params& params, int32_t B, int64_t max_len, const DeviceInfo& info,
+                  void* ws, hipStream_t stream) {
+  ets::Params p = params;
+  p.min_chunk = min_chunk_setting();
   const Shape sh = launch_shape(B, max_len, info);
   if (sh.groups == 1) {
     if (sh.threads == 512) {
@@ -2376,6 +2409,7 @@ ets_status ets_floor_read(const float* scores, int64_t row_stride, int32_t B, in
   p.lens = lens;
   p.row_starts = row_starts;
   p.L = L;
+  p.min_chunk = min_chunk_setting();
   auto s = static_cast<hipStream_t>(stream);
   const uint32_t g = static_cast<uint32_t>(grid);
   if (ragged) {

@@ -236,6 +236,14 @@ int32_t ets_group_cap(int32_t cu_count, int32_t xcd_count, int32_t groups_per_cu
  * ets_workspace_size and the floors then return ETS_ERR_INVALID_ARG.  After
  * the pages' row_split heuristic (PR #37591 digest, the topk.hip excerpt),
  * with constants of this library measured on MI355X.
+ *
+ * A split row of n scores gives each member a chunk of ceil(n / G) scores,
+ * rounded up to a multiple of 4, but at least 4096 (enough for a member to
+ * bound the row's k-th largest), so a row shorter than G * 4096 leaves its
+ * last members empty.  The environment variable ETS_MIN_CHUNK, when set to an
+ * integer >= 1, replaces that 4096 (rounded up to a multiple of 4, at most
+ * 32768; read at every call).  It changes the work division only, never the
+ * result.
  */
 int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count, int32_t max_group);
 

@@ -22,16 +22,25 @@ pytestmark = pytest.mark.gpu
 
 
 @contextlib.contextmanager
-def split(g):
-    old = os.environ.get("ETS_ROW_SPLIT")
+def split(g, min_chunk=4):
+    """Forces g workgroups per row.  min_chunk (ETS_MIN_CHUNK, default 4)
+    sets the fewest scores per member chunk: 4 divides even short rows
+    among all g members, which the geometry tests below rely on; None keeps
+    the library's default (4096)."""
+    saved = {v: os.environ.get(v) for v in ("ETS_ROW_SPLIT", "ETS_MIN_CHUNK")}
     os.environ["ETS_ROW_SPLIT"] = str(g)
+    if min_chunk is None:
+        os.environ.pop("ETS_MIN_CHUNK", None)
+    else:
+        os.environ["ETS_MIN_CHUNK"] = str(min_chunk)
     try:
         yield
     finally:
-        if old is None:
-            os.environ.pop("ETS_ROW_SPLIT", None)
-        else:
-            os.environ["ETS_ROW_SPLIT"] = old
+        for v, old in saved.items():
+            if old is None:
+                os.environ.pop(v, None)
+            else:
+                os.environ[v] = old
 
 
 def _raw(name, x, k, lens=None):
@@ -258,6 +267,37 @@ def test_ragged_row_edges(first_lead):
             with split(g):
                 print("first_lead", first_lead, "k", k, "G", g, flush=True)
                 assert_parity(w, run_gpu(w), want)
+
+
+@pytest.mark.parametrize("k", [64, 2048])
+def test_default_min_chunk_leaves_members_empty(k):
+    """With the library's fewest scores per chunk (4096), a 16-way split of
+    rows shorter than 16 * 4096 gives each row ceil(n / 4096) non-empty
+    members and leaves the rest empty; rows longer than that are divided
+    evenly.  Both must match the oracle."""
+    rng = np.random.default_rng(77 + k)
+    L = 81920
+    lens = np.array([k + 1, 4095, 4096, 4097, 12289, 40964, 65536, 65537, L], dtype=np.int32)
+    x = rng.standard_normal((lens.size, L)).astype(np.float32)
+    x[3, 4096] = 1e9  # the only score of the second member of a 4097-score row
+    w = _raw("min-chunk", x, k, lens)
+    want = run_oracle(w)
+    for g in (2, 16, 20):
+        with split(g, min_chunk=None):
+            assert_parity(w, run_gpu(w), want)
+
+
+def test_spread_lengths_at_the_default_split():
+    """Long raw rows whose lengths spread far below the longest (the host
+    sees only the longest): the default split and chunking against the
+    oracle."""
+    rng = np.random.Generator(np.random.PCG64(1008))
+    B, L, k = 4, 262144, 2048
+    x = workloads.normal_dense(rng, B, L)
+    lens = rng.integers(L // 8, L, size=B, endpoint=True).astype(np.int32)
+    lens[0] = L // 8
+    w = _raw("spread", x, k, lens)
+    assert_parity(w, run_gpu(w), run_oracle(w))
 
 
 def test_one_workspace_across_shapes_and_apis():
