@@ -240,6 +240,10 @@ def main() -> int:
                          "workgroups per row (ETS_ROW_SPLIT)")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a HIP graph")
+    ap.add_argument("--host-overhead", action="store_true",
+                    help="instead of the headline: host time per eager call of the headline "
+                         "workload, through the Python binding and as a direct C call with "
+                         "prepared arguments (one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain device copy of known size (counter calibration) and exit")
     ap.add_argument("--traffic-report", metavar="DIR",
@@ -265,6 +269,8 @@ def main() -> int:
         return calibrate_copy(torch, args.steps)
     if args.sweep:
         return sweep(torch, ets, workloads, args)
+    if args.host_overhead:
+        return host_overhead(torch, ets, workloads, args)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -425,6 +431,50 @@ def sweep(torch, ets, workloads, args) -> int:
               flush=True)
         del rig
         torch.cuda.empty_cache()
+    return 0
+
+
+def host_overhead(torch, ets, workloads, args) -> int:
+    """Host microseconds per eager call: the loop's time before the stream is
+    drained (host-bound when above the kernel's time), and with the drain."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.make(args.workload, seed=args.seed)
+    if w.api != "paged":
+        raise SystemExit("--host-overhead times the paged call (C1, C2, C3)")
+    s = torch.from_numpy(w.scores).to(dev)
+    lens = torch.from_numpy(w.lens).to(dev)
+    pt = torch.from_numpy(w.page_table).to(dev)
+    out = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+    ws = ets.new_workspace(w.B, w.L, w.k, dev)
+    n = max(args.steps, 3000)
+    lib = ets._load()
+    prepared = (s.data_ptr(), s.stride(0), w.B, w.L, lens.data_ptr(), pt.data_ptr(), pt.stride(0),
+                w.page_size, w.k, out.data_ptr(), out.stride(0),
+                ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+                torch.cuda.current_stream(dev).cuda_stream)
+
+    def binding():
+        ets.topk_paged(s, lens, pt, out, w.page_size, workspace=ws)
+
+    def direct():
+        lib.ets_topk_paged(*prepared)
+
+    res = {}
+    for name, f in (("binding", binding), ("direct_c", direct)):
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            f()
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        res[name] = {"host_us_per_call": (t1 - t0) / n * 1e6,
+                     "us_per_call_with_drain": (t2 - t0) / n * 1e6}
+    print(json.dumps({"host_overhead": res, "workload": w.name, "calls": n,
+                      "eager_launches": True}), flush=True)
     return 0
 
 

@@ -101,22 +101,27 @@ def _check(status: int, what: str) -> None:
         raise EtsError(status, what)
 
 
+# The per-call checks below use only cheap tensor attributes (a decode step
+# makes tens of calls, and an eager call's host time is all overhead).
+
 def _require(t: torch.Tensor, name: str, dtype: torch.dtype, dim: int) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if t.dtype != dtype:
+    if t.dtype is not dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    if t.dim() != dim:
+    if t.ndim != dim:
         raise ValueError("%s must be %d-D, got shape %s" % (name, dim, tuple(t.shape)))
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be on a HIP device, got %s" % (name, t.device))
 
 
 def _rows(t: torch.Tensor, name: str) -> int:
     """Row stride (elements) of a 2-D tensor whose rows are contiguous."""
-    if t.shape[1] > 1 and t.stride(1) != 1:
+    rows, cols = t.shape
+    st0, st1 = t.stride()
+    if cols > 1 and st1 != 1:
         raise ValueError("%s rows must be contiguous (stride(1) == 1)" % name)
-    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+    return st0 if rows > 1 else max(cols, 1)
 
 
 def _vec(t: torch.Tensor, name: str, n: int) -> None:
@@ -127,8 +132,32 @@ def _vec(t: torch.Tensor, name: str, n: int) -> None:
         raise ValueError("%s must be contiguous" % name)
 
 
-def _stream(device: torch.device) -> int:
-    return torch.cuda.current_stream(device).cuda_stream
+def _same_device(index: int, *named) -> None:
+    for t, nm in named:
+        if t is not None and t.get_device() != index:
+            raise ValueError("%s must be on cuda:%d" % (nm, index))
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device) -> int:
+    """Handle of torch's current stream on a device (index or torch.device)."""
+    index = device if isinstance(device, int) else device.index
+    if index is None:
+        index = torch.cuda.current_device()
+    if _raw_stream is not None:
+        return _raw_stream(index)
+    return torch.cuda.current_stream(index).cuda_stream
+
+
+def _on(index: int, fn, *args):
+    """fn(*args) with device `index` current (the C calls act on the current
+    device); switches only when another device is current."""
+    if torch.cuda.current_device() == index:
+        return fn(*args)
+    with torch.cuda.device(index):
+        return fn(*args)
 
 
 def workspace_size(B: int, max_row_len: int, k: int, device: Optional[int] = None) -> int:
@@ -221,40 +250,67 @@ def workspace_error(workspace: Optional[torch.Tensor]) -> int:
     return int(flag.item())
 
 
-def _workspace(B: int, max_len: int, k: int, device: torch.device,
-               workspace: Optional[torch.Tensor]):
-    with torch.cuda.device(device):
-        need = workspace_size(B, max_len, k)
-    if need == 0:
-        return None, 0
-    if workspace is None:
-        if torch.cuda.is_current_stream_capturing():
-            # a captured graph keeps the buffer's address for its replays, and
-            # the shared buffer may be replaced by a larger one later
+ETS_ERR_WORKSPACE = 3
+
+
+def _select(what: str, fn, args: tuple, index: int, B: int, max_len: int, k: int,
+            workspace: Optional[torch.Tensor]) -> None:
+    """Runs one selection call fn(*args, workspace, workspace_bytes, stream) on
+    device `index`.  The library reports a missing or short workspace before
+    enqueueing anything (ETS_ERR_WORKSPACE), so the common call makes one C
+    call: with the caller's workspace, or with the one kept for this device
+    and stream (created, or grown, only when a call asks for it)."""
+    stream = _stream(index)
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+            raise TypeError("workspace must be a torch.Tensor on a HIP device")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        _same_device(index, (workspace, "workspace"))
+        nbytes = workspace.numel() * workspace.element_size()
+        st = _on(index, fn, *args, workspace.data_ptr(), nbytes, stream)
+        if st == ETS_ERR_WORKSPACE:
+            need = _on(index, workspace_size, B, max_len, k)
+            raise ValueError("workspace must hold at least %d bytes, 16-byte aligned (got %d)"
+                             % (need, nbytes))
+        _check(st, what)
+        return
+    # a captured graph keeps a buffer's address for its replays, and the
+    # shared buffer may be replaced by a larger one later: none under capture
+    capturing = torch.cuda.is_current_stream_capturing()
+    key = (index, stream)
+    ws = None if capturing else _ws_cache.get(key)
+    st = _on(index, fn, *args, ws.data_ptr() if ws is not None else None,
+             ws.numel() if ws is not None else 0, stream)
+    if st == ETS_ERR_WORKSPACE:
+        need = _on(index, workspace_size, B, max_len, k)
+        if capturing:
             raise ValueError("a call that needs a workspace (%d bytes) must be given one "
                              "while a graph is being captured: pass workspace=new_workspace(...)"
                              % need)
-        key = (device.index, _stream(device))
         with _lock:
-            workspace = _ws_cache.get(key)
-            if workspace is None or workspace.numel() < need:
-                with torch.cuda.device(device):
-                    workspace = torch.zeros(need, dtype=torch.uint8, device=device)
-                _ws_cache[key] = workspace
-    if workspace.device != device or workspace.numel() * workspace.element_size() < need:
-        raise ValueError("workspace must be on %s with at least %d bytes" % (device, need))
-    return workspace, workspace.numel() * workspace.element_size()
+            ws = _ws_cache.get(key)
+            if ws is None or ws.numel() < need:
+                ws = torch.zeros(need, dtype=torch.uint8, device=torch.device("cuda", index))
+                _ws_cache[key] = ws
+        st = _on(index, fn, *args, ws.data_ptr(), ws.numel(), stream)
+    _check(st, what)
 
 
-def _out(out: Optional[torch.Tensor], B: int, k: int, device: torch.device) -> torch.Tensor:
+def _out(out: Optional[torch.Tensor], B: int, k: int, index: int) -> torch.Tensor:
     if out is None:
-        return torch.empty((B, k), dtype=torch.int32, device=device)
+        return torch.empty((B, k), dtype=torch.int32, device=torch.device("cuda", index))
     _require(out, "out", torch.int32, 2)
-    if out.shape[0] != B or out.shape[1] < k or out.device != device:
-        raise ValueError("out must be int32 [B, >=k] on %s" % device)
+    rows, cols = out.shape
+    if rows != B or cols < k or out.get_device() != index:
+        raise ValueError("out must be int32 [B, >=k] on cuda:%d" % index)
     if k > 1 and out.stride(1) != 1:
         raise ValueError("out rows must be contiguous")
     return out
+
+
+def _out_stride(out: torch.Tensor, B: int, k: int) -> int:
+    return out.stride(0) if B > 1 else k
 
 
 def topk_raw(scores: torch.Tensor, k: int, lens: Optional[torch.Tensor] = None,
@@ -263,20 +319,15 @@ def topk_raw(scores: torch.Tensor, k: int, lens: Optional[torch.Tensor] = None,
     """Exact top-k positions of each row of fp32 ``scores`` [B, L]; int32 [B, k]."""
     _require(scores, "scores", torch.float32, 2)
     B, L = scores.shape
-    dev = scores.device
+    index = scores.get_device()
     if lens is not None:
         _vec(lens, "lens", B)
-        if lens.device != dev:
-            raise ValueError("lens must be on %s" % dev)
-    out = _out(out, B, k, dev)
-    ws, ws_bytes = _workspace(B, L, k, dev, workspace)
-    with torch.cuda.device(dev):
-        st = _load().ets_topk_raw(scores.data_ptr(), _rows(scores, "scores"), B, L,
-                                  lens.data_ptr() if lens is not None else None, k,
-                                  out.data_ptr(), out.stride(0) if B > 1 else k,
-                                  ws.data_ptr() if ws is not None else None, ws_bytes,
-                                  _stream(dev))
-    _check(st, "ets_topk_raw")
+        _same_device(index, (lens, "lens"))
+    out = _out(out, B, k, index)
+    args = (scores.data_ptr(), _rows(scores, "scores"), B, L,
+            lens.data_ptr() if lens is not None else None, k, out.data_ptr(),
+            _out_stride(out, B, k))
+    _select("ets_topk_raw", _load().ets_topk_raw, args, index, B, L, k, workspace)
     return out
 
 
@@ -291,47 +342,44 @@ def topk_paged(scores: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.T
     (int32 [B]) row b selects among positions [window_starts[b], seq_lens[b])
     only (ets_topk_paged_window).
     """
+    index, B, L, k = _paged_checks(scores, seq_lens, page_table, page_indices, page_size)
+    lib = _load()
+    if window_starts is None:
+        args = (scores.data_ptr(), _rows(scores, "scores"), B, L, seq_lens.data_ptr(),
+                page_table.data_ptr(), _rows(page_table, "page_table"), page_size, k,
+                page_indices.data_ptr(), _out_stride(page_indices, B, k))
+        _select("ets_topk_paged", lib.ets_topk_paged, args, index, B, L, k, workspace)
+    else:
+        _vec(window_starts, "window_starts", B)
+        _same_device(index, (window_starts, "window_starts"))
+        args = (scores.data_ptr(), _rows(scores, "scores"), B, L, window_starts.data_ptr(),
+                seq_lens.data_ptr(), page_table.data_ptr(), _rows(page_table, "page_table"),
+                page_size, k, page_indices.data_ptr(), _out_stride(page_indices, B, k))
+        _select("ets_topk_paged_window", lib.ets_topk_paged_window, args, index, B, L, k,
+                workspace)
+    return page_indices
+
+
+def _paged_checks(scores, seq_lens, page_table, page_indices, page_size):
+    """Checks shared by the paged calls; returns (device index, B, L, k)."""
     _require(scores, "scores", torch.float32, 2)
     B, L = scores.shape
-    dev = scores.device
+    index = scores.get_device()
     _vec(seq_lens, "seq_lens", B)
     _require(page_table, "page_table", torch.int32, 2)
-    if page_table.shape[0] != B:
+    pt_rows, pt_pages = page_table.shape
+    if pt_rows != B:
         raise ValueError("page_table must have B rows")
     _require(page_indices, "page_indices", torch.int32, 2)
     k = page_indices.shape[1]
-    out = _out(page_indices, B, k, dev)
-    for t, nm in ((seq_lens, "seq_lens"), (page_table, "page_table")):
-        if t.device != dev:
-            raise ValueError("%s must be on %s" % (nm, dev))
+    _out(page_indices, B, k, index)
+    _same_device(index, (seq_lens, "seq_lens"), (page_table, "page_table"))
     if page_size < 1:
         raise ValueError("page_size must be >= 1")
-    if page_table.shape[1] * page_size < L:
+    if pt_pages * page_size < L:
         raise ValueError("page_table has %d pages of %d, fewer than L = %d positions"
-                         % (page_table.shape[1], page_size, L))
-    if window_starts is not None:
-        _vec(window_starts, "window_starts", B)
-        if window_starts.device != dev:
-            raise ValueError("window_starts must be on %s" % dev)
-    ws, ws_bytes = _workspace(B, L, k, dev, workspace)
-    with torch.cuda.device(dev):
-        if window_starts is None:
-            st = _load().ets_topk_paged(scores.data_ptr(), _rows(scores, "scores"), B, L,
-                                        seq_lens.data_ptr(), page_table.data_ptr(),
-                                        _rows(page_table, "page_table"), page_size, k,
-                                        out.data_ptr(), out.stride(0) if B > 1 else k,
-                                        ws.data_ptr() if ws is not None else None, ws_bytes,
-                                        _stream(dev))
-        else:
-            st = _load().ets_topk_paged_window(scores.data_ptr(), _rows(scores, "scores"), B, L,
-                                               window_starts.data_ptr(), seq_lens.data_ptr(),
-                                               page_table.data_ptr(),
-                                               _rows(page_table, "page_table"), page_size, k,
-                                               out.data_ptr(), out.stride(0) if B > 1 else k,
-                                               ws.data_ptr() if ws is not None else None,
-                                               ws_bytes, _stream(dev))
-    _check(st, "ets_topk_paged" if window_starts is None else "ets_topk_paged_window")
-    return out
+                         % (pt_pages, page_size, L))
+    return index, B, L, k
 
 
 def topk_paged_noalloc(scores: torch.Tensor, seq_lens: torch.Tensor, page_table: torch.Tensor,
@@ -341,37 +389,17 @@ def topk_paged_noalloc(scores: torch.Tensor, seq_lens: torch.Tensor, page_table:
     per-device scratch (4 MiB), so the call allocates nothing, here or in the
     library.  Calls that may overlap on one device race.  ``error_flag``
     (int32 [>=1], optional) receives the scratch's error word."""
-    _require(scores, "scores", torch.float32, 2)
-    B, L = scores.shape
-    dev = scores.device
-    _vec(seq_lens, "seq_lens", B)
-    _require(page_table, "page_table", torch.int32, 2)
-    if page_table.shape[0] != B:
-        raise ValueError("page_table must have B rows")
-    _require(page_indices, "page_indices", torch.int32, 2)
-    k = page_indices.shape[1]
-    out = _out(page_indices, B, k, dev)
-    for t, nm in ((seq_lens, "seq_lens"), (page_table, "page_table")):
-        if t.device != dev:
-            raise ValueError("%s must be on %s" % (nm, dev))
-    if page_size < 1:
-        raise ValueError("page_size must be >= 1")
-    if page_table.shape[1] * page_size < L:
-        raise ValueError("page_table has %d pages of %d, fewer than L = %d positions"
-                         % (page_table.shape[1], page_size, L))
+    index, B, L, k = _paged_checks(scores, seq_lens, page_table, page_indices, page_size)
     if error_flag is not None:
         _require(error_flag, "error_flag", torch.int32, 1)
-        if error_flag.device != dev or error_flag.numel() < 1:
-            raise ValueError("error_flag must be int32 [>=1] on %s" % dev)
-    with torch.cuda.device(dev):
-        st = _load().ets_topk_paged_noalloc(scores.data_ptr(), _rows(scores, "scores"), B, L,
-                                            seq_lens.data_ptr(), page_table.data_ptr(),
-                                            _rows(page_table, "page_table"), page_size, k,
-                                            out.data_ptr(), out.stride(0) if B > 1 else k,
-                                            error_flag.data_ptr() if error_flag is not None
-                                            else None, _stream(dev))
+        if error_flag.get_device() != index or error_flag.numel() < 1:
+            raise ValueError("error_flag must be int32 [>=1] on cuda:%d" % index)
+    st = _on(index, _load().ets_topk_paged_noalloc, scores.data_ptr(), _rows(scores, "scores"),
+             B, L, seq_lens.data_ptr(), page_table.data_ptr(), _rows(page_table, "page_table"),
+             page_size, k, page_indices.data_ptr(), _out_stride(page_indices, B, k),
+             error_flag.data_ptr() if error_flag is not None else None, _stream(index))
     _check(st, "ets_topk_paged_noalloc")
-    return out
+    return page_indices
 
 
 def topk_ragged(packed: torch.Tensor, row_starts: torch.Tensor, lengths: torch.Tensor, k: int,
@@ -383,23 +411,20 @@ def topk_ragged(packed: torch.Tensor, row_starts: torch.Tensor, lengths: torch.T
     which synchronises the stream.
     """
     _require(packed, "packed", torch.float32, 1)
-    dev = packed.device
+    index = packed.get_device()
+    _require(row_starts, "row_starts", torch.int32, 1)
     B = row_starts.shape[0]
     _vec(row_starts, "row_starts", B)
     _vec(lengths, "lengths", B)
+    _same_device(index, (row_starts, "row_starts"), (lengths, "lengths"))
     if packed.numel() > 1 and packed.stride(0) != 1:
         raise ValueError("packed must be contiguous")
     if max_len is None:
         max_len = int(lengths.max().item()) if B else 0
-    out = _out(out, B, k, dev)
-    ws, ws_bytes = _workspace(B, max_len, k, dev, workspace)
-    with torch.cuda.device(dev):
-        st = _load().ets_topk_ragged(packed.data_ptr(), row_starts.data_ptr(),
-                                     lengths.data_ptr(), B, max_len, k, out.data_ptr(),
-                                     out.stride(0) if B > 1 else k,
-                                     ws.data_ptr() if ws is not None else None, ws_bytes,
-                                     _stream(dev))
-    _check(st, "ets_topk_ragged")
+    out = _out(out, B, k, index)
+    args = (packed.data_ptr(), row_starts.data_ptr(), lengths.data_ptr(), B, max_len, k,
+            out.data_ptr(), _out_stride(out, B, k))
+    _select("ets_topk_ragged", _load().ets_topk_ragged, args, index, B, max_len, k, workspace)
     return out
 
 
