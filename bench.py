@@ -254,8 +254,9 @@ def main() -> int:
         return traffic_report(args.traffic_report, args.workload, args.seed)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the top-k rows are independent and this build "
-              "has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the top-k rows are independent, so a batch "
+              "shards across GPUs by row blocks with no exchange, and the library has no "
+              "multi-GPU path of its own (run with --gpus 1)", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
