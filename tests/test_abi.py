@@ -217,3 +217,13 @@ def test_row_split_bounds_hold_everywhere():
     finally:
         if env is not None:
             os.environ["ETS_ROW_SPLIT"] = env
+
+
+def test_binding_constants_match_the_header():
+    """The binding's copies of the header's limits."""
+    import exact_top_selection_amd as ets
+    text = open(HEADER).read()
+    max_k = int(re.search(r"#define ETS_MAX_K (\d+)", text).group(1))
+    scratch = re.search(r"#define ETS_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert ets.MAX_K == max_k
+    assert ets.NOALLOC_SCRATCH_BYTES == int(scratch.group(1)) << int(scratch.group(2))

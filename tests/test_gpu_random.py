@@ -1,6 +1,7 @@
-"""Randomised GPU parity: every entry point on seeded random shapes, lengths,
-value distributions, page sizes, windows and forced row splits, each compared
-with the oracle (bit-exact sorted index sets and equal value multisets).
+"""Randomised GPU parity: every entry point (the allocation-free paged call
+included) on seeded random shapes, lengths, value distributions, page sizes,
+windows and forced row splits, each compared with the oracle (bit-exact
+sorted index sets and equal value multisets).
 
 random_case(seed) draws one valid call from its seed alone, so a failing case
 is named by its seed.  The cases cover what the method has to handle exactly
@@ -105,6 +106,8 @@ def random_case(seed):
     pt = np.stack([rng.permutation(P) + int(rng.integers(0, 1000)) for _ in range(B)]).astype(np.int32)
     w = Workload(name, "paged", k, B, x, L=L, lens=lens, page_table=pt, page_size=ps)
     wins = rng.integers(-5, L + 6, size=B).astype(np.int32) if api == "window" else None
+    if wins is None and rng.random() < 0.3:
+        w.extra["noalloc"] = True  # through ets_topk_paged_noalloc
     return w, env, wins
 
 
@@ -153,7 +156,7 @@ def run_case(seed):
     cu, _, cap = ets.device_limits()
     if "ETS_ROW_SPLIT" in env and int(env["ETS_ROW_SPLIT"]) > cap:
         env["ETS_ROW_SPLIT"] = str(cap)
-    print("case", w.name, env, flush=True)
+    print("case", w.name, env, "noalloc" if w.extra.get("noalloc") else "", flush=True)
     d = dev()
     out = torch.full((w.B, w.k), POISON, dtype=torch.int32, device=d)
     s = torch.from_numpy(w.scores).to(d)
@@ -164,6 +167,19 @@ def run_case(seed):
             ets.topk_ragged(s, torch.from_numpy(w.row_starts).to(d),
                             torch.from_numpy(w.lengths).to(d), w.k, max_len=max(w.max_len, 0),
                             out=out)
+        elif w.extra.get("noalloc"):
+            flag = torch.full((1,), -1, dtype=torch.int32, device=d)
+            try:
+                ets.topk_paged_noalloc(s, torch.from_numpy(w.lens).to(d),
+                                       torch.from_numpy(w.page_table).to(d), out, w.page_size,
+                                       error_flag=flag)
+            except ets.EtsError as e:
+                # only a split call whose workspace exceeds the static scratch
+                need = ets.workspace_size(w.B, w.L, w.k)
+                assert e.status == 6 and need > ets.NOALLOC_SCRATCH_BYTES, (e.status, need)
+                return
+            torch.cuda.synchronize(d)
+            assert int(flag.item()) == 0, "a row group stopped waiting"
         else:
             ets.topk_paged(s, torch.from_numpy(w.lens).to(d), torch.from_numpy(w.page_table).to(d),
                            out, w.page_size,
