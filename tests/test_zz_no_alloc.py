@@ -95,3 +95,51 @@ def test_noalloc_rejects_shapes_beyond_the_scratch():
     assert b"scratch" in lib.ets_status_string(ETS_ERR_SCRATCH)
     torch.cuda.synchronize()
     assert int((out != 9).sum().item()) == 0
+
+
+def test_noalloc_graph_replays_match_the_oracle():
+    """Split calls captured in a HIP graph use the static scratch on every
+    replay: four replays, each after an eager call of another shape on the
+    same stream (which leaves the scratch zero in between), all equal the
+    oracle, with the error flag at zero."""
+    d = torch.device("cuda:0")
+    cu, _, cap = ets.device_limits()
+    w = _case(81, 4, 70000, 1024)
+    other = _case(82, 3, 131072, 2048)
+    for c in (w, other):
+        assert ets.row_split(c.B, c.L, cu, cap) > 0
+    want = run_oracle(w)
+    want_other = run_oracle(other)
+    s = torch.from_numpy(w.scores).to(d)
+    lens = torch.from_numpy(w.lens).to(d)
+    pt = torch.from_numpy(w.page_table).to(d)
+    out = torch.full((w.B, w.k), 7, dtype=torch.int32, device=d)
+    flag = torch.full((1,), -1, dtype=torch.int32, device=d)
+    s2 = torch.from_numpy(other.scores).to(d)
+    lens2 = torch.from_numpy(other.lens).to(d)
+    pt2 = torch.from_numpy(other.page_table).to(d)
+    out2 = torch.full((other.B, other.k), 7, dtype=torch.int32, device=d)
+    flag2 = torch.full((1,), -1, dtype=torch.int32, device=d)
+    # one eager call first, so that the scratch has been zero-filled outside capture
+    ets.topk_paged_noalloc(s, lens, pt, out, w.page_size, error_flag=flag)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            ets.topk_paged_noalloc(s, lens, pt, out, w.page_size, error_flag=flag)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        print("noalloc graph replay", rep, flush=True)
+        out.fill_(7)
+        flag.fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 0
+        _same_sets(out.cpu().numpy(), want)
+        out2.fill_(7)
+        ets.topk_paged_noalloc(s2, lens2, pt2, out2, other.page_size, error_flag=flag2)
+        torch.cuda.synchronize()
+        assert int(flag2.item()) == 0
+        _same_sets(out2.cpu().numpy(), want_other)
