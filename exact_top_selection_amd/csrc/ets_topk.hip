@@ -1258,8 +1258,9 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // the next ticket.  With G above one XCD's slots the incomplete group can
 // hold every slot of the last XCD while its missing members are queued
 // behind them there: a wait then runs to its bound.  Every wait is bounded;
-// on expiry the workspace's error word is set, the call's output is
-// undefined, and the kernel still ends.
+// on expiry the workspace's error word gets the bit of that wait (bounds
+// exchange, coarse table or round barrier), the call's output is undefined,
+// and the kernel still ends.
 
 // Data crosses workgroups only through agent-scope relaxed atomics, with each
 // wave's memory counter drained before an arrival is counted (or, for the
@@ -1315,6 +1316,8 @@ constexpr int kHdrWords = 64;
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 enum HdrField : int { kHdrTicket = 0, kHdrFinished = 16, kHdrError = 32 };
+// Bits of the error word: which bounded wait ran out, or a stale ticket.
+enum ErrBit : uint32_t { kErrBounds = 1u, kErrStale = 2u, kErrCoarse = 4u, kErrBarrier = 8u };
 enum GroupRecField : int { kRecBarrier = 0, kRecDone = 16, kRecCursor = 32 /* u64 */,
                           kRecBelow = 48, kRecSlots = 64 /* u64 per member */ };
 
@@ -1337,6 +1340,9 @@ __device__ __forceinline__ U add_dev(U* p, U v) {
 __device__ __forceinline__ void max_dev(uint32_t* p, uint32_t v) {
   __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void or_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Waits until every global access this wave issued has completed.
 __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -1353,7 +1359,7 @@ __device__ __forceinline__ void group_sync(uint32_t* ctr, uint32_t target, uint3
       __builtin_amdgcn_s_sleep(1);
       seen = ld_dev(ctr);
       if (++spins > kSpinLimit) {
-        st_dev(err, 1u);
+        or_dev(err, kErrBarrier);
         break;
       }
     }
@@ -1442,7 +1448,8 @@ __device__ __forceinline__ uint32_t push_coarse(uint32_t* lh, uint32_t* dst) {
 // word only grows, so the total reaches n exactly when every member's adds
 // have landed, and then every word is final.  Then finds the threshold bin
 // for kk: (bin, entries above it, entries in it), the same in every lane.  A
-// wait past kSpinLimit polls sets the error flag and returns what it read.
+// wait past kSpinLimit polls sets kErrCoarse in the error word and returns
+// what it read.
 __device__ __forceinline__ uint3 poll_coarse(const uint32_t* src, const uint32_t* below, uint32_t n,
                                              uint32_t kk, uint32_t* err) {
   constexpr int C = kCoarseBins / 64;  // coarse bins per lane
@@ -1468,7 +1475,7 @@ __device__ __forceinline__ uint3 poll_coarse(const uint32_t* src, const uint32_t
     const uint32_t total = wave_reduce(sum, OpAdd()) + b;
     if (total == n) break;
     if (spins > kSpinLimit) {
-      if (l == 0) st_dev(err, 1u);
+      if (l == 0) or_dev(err, kErrCoarse);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -1622,7 +1629,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
         __builtin_amdgcn_s_sleep(1);
         v = ld_dev(slots + tid);
         if (++spins > kSpinLimit) {
-          st_dev(err, 1u);
+          or_dev(err, kErrBounds);
           break;
         }
       }
@@ -1951,7 +1958,7 @@ __global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, i
   if (b >= B) {
     // only a workspace that was not zero (a stale ticket) gets here: this
     // workgroup's chunk goes unselected, so the call's output is undefined
-    if (threadIdx.x == 0) st_dev(w.hdr + kHdrError, 2u);
+    if (threadIdx.x == 0) or_dev(w.hdr + kHdrError, kErrStale);
   } else {
     const RowRef<MODE> r(p, b);
     if (r.n <= p.k) {

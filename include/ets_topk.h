@@ -197,8 +197,11 @@ ets_status ets_workspace_init(void* workspace, size_t bytes, void* stream);
  * Enqueues on `stream` a copy of the workspace's error word into flag[0]
  * (device int32, caller-owned) and clears the word, so that the next calls
  * start clean.  Non-zero means a call before it on the stream stopped waiting
- * for the other workgroups of a row (1: a bounded wait ran out; 2: a stale
- * ticket in a workspace that was not zero) and its output is undefined.
+ * for the other workgroups of a row, and its output is undefined.  The word
+ * is an OR of bits: 2 marks a stale ticket (a workspace that was not zero);
+ * the others name the bounded wait that ran out: 1 the exchange of the row's
+ * bounds, 4 the poll of the row's coarse histogram, 8 a barrier between
+ * radix rounds.
  * workspace_bytes = 0 (a call that needed no workspace) writes 0; otherwise
  * workspace must be 16-byte aligned and at least 256 bytes.  Nothing is
  * synchronised: read flag after the stream reaches it.

@@ -227,3 +227,21 @@ def test_binding_constants_match_the_header():
     scratch = re.search(r"#define ETS_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert ets.MAX_K == max_k
     assert ets.NOALLOC_SCRATCH_BYTES == int(scratch.group(1)) << int(scratch.group(2))
+
+
+def test_error_bits_match_the_header_and_the_kernels():
+    """The error word's bits: the binding's table, the header's description
+    and the kernel source's enum name the same values."""
+    import exact_top_selection_amd as ets
+    text = " ".join(open(HEADER).read().replace("\n *", "\n").split())
+    assert "2 marks a stale ticket" in text
+    for bit, words in ((1, "the exchange of the row's bounds"), (4, "the poll of the row's coarse histogram"),
+                       (8, "a barrier between radix rounds")):
+        assert "%d %s" % (bit, words) in text, bit
+    src = open(os.path.join(ROOT, "exact_top_selection_amd", "csrc", "ets_topk.hip")).read()
+    enum = re.search(r"enum ErrBit : uint32_t \{([^}]*)\}", src).group(1)
+    vals = {name.strip(): int(v.strip().rstrip("u"), 0) for name, v in
+            (item.split("=") for item in enum.split(","))}
+    assert vals == {"kErrBounds": 1, "kErrStale": 2, "kErrCoarse": 4, "kErrBarrier": 8}
+    assert sorted(ets.ERROR_BITS) == [1, 2, 4, 8]
+    assert ets.ERROR_BITS[2] == "stale ticket"

@@ -179,14 +179,16 @@ def run_case(seed):
                 assert e.status == 6 and need > ets.NOALLOC_SCRATCH_BYTES, (e.status, need)
                 return
             torch.cuda.synchronize(d)
-            assert int(flag.item()) == 0, "a row group stopped waiting"
+            e = int(flag.item())
+            assert e == 0, "a row group stopped waiting (error word %d)" % e
         else:
             ets.topk_paged(s, torch.from_numpy(w.lens).to(d), torch.from_numpy(w.page_table).to(d),
                            out, w.page_size,
                            window_starts=None if wins is None else torch.from_numpy(wins).to(d))
         torch.cuda.synchronize(d)
     for ws in ets._ws_cache.values():
-        assert ets.workspace_error(ws) == 0, "a row group stopped waiting"
+        e = ets.workspace_error(ws)
+        assert e == 0, "a row group stopped waiting (error word %d)" % e
     got = out.cpu().numpy()
     want = _oracle(w, wins)
     if wins is None:

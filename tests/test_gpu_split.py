@@ -52,7 +52,8 @@ def _assert_clean(ws):
     """The error word is zero, and so are the counters and histogram tables a
     call relies on; the tie lists behind them may keep stale entries."""
     torch.cuda.synchronize()
-    assert ets.workspace_error(ws) == 0, "a call stopped waiting for its row group"
+    e = ets.workspace_error(ws)
+    assert e == 0, "a call stopped waiting for its row group (error word %d)" % e
     nz = workspace_dirty(ws)
     assert nz == 0, "%d counter or table words left non-zero" % nz
 
@@ -69,7 +70,8 @@ def _error_words_stay_zero():
         ets.workspace_error(ws)
     yield
     for ws in _cached_workspaces():
-        assert ets.workspace_error(ws) == 0, "a call stopped waiting for its row group"
+        e = ets.workspace_error(ws)
+        assert e == 0, "a call stopped waiting for its row group (error word %d)" % e
 
 
 _G64 = pytest.param(64, marks=pytest.mark.skip(
@@ -379,7 +381,8 @@ def test_large_row_group_grids():
             ws = ets.new_workspace(B, L, k, d)
             for _ in range(4):
                 ets.topk_raw(s, k, None, out=out, workspace=ws)
-                assert ets.workspace_error(ws) == 0, "a call stopped waiting for its row group"
+                e = ets.workspace_error(ws)
+                assert e == 0, "a call stopped waiting for its row group (error word %d)" % e
         w = _raw("large-grid", x, k)
         assert_parity(w, out.cpu().numpy(), run_oracle(w))
         _assert_clean(ws)
