@@ -275,12 +275,12 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cu, _, cap = ets.device_limits()
+    limits = ets.device_limits()
     aux_steps = max(args.steps, 200)  # floors and per-config lines
 
     # ---- the headline workload
     w = workloads.make(args.workload, seed=args.seed)
-    rig = Rig(torch, ets, w, dev, cu, cap)
+    rig = Rig(torch, ets, w, dev, limits)
     ms_total = timed(torch, rig.step, args.steps, args.warmup, args.eager)
     us_per_step = ms_total * 1e3 / args.steps
     rows_per_s = w.B / (us_per_step * 1e-6)
@@ -330,7 +330,7 @@ def main() -> int:
         per = {}
         for name in workloads.NAMES:
             wc = workloads.make(name, seed=args.seed)
-            rc = Rig(torch, ets, wc, dev, cu, cap)
+            rc = Rig(torch, ets, wc, dev, limits)
             us = timed(torch, rc.step, aux_steps, args.warmup, args.eager) * 1e3 / aux_steps
             ab = algorithmic_bytes(wc)
             gbs = ab / (us * 1e-6) / 1e9
@@ -348,7 +348,7 @@ def main() -> int:
     return 0
 
 
-def sweep_spread(torch, ets, workloads, args, dev, cu, cap, steps) -> int:
+def sweep_spread(torch, ets, workloads, args, dev, limits, steps) -> int:
     """The split heuristic sees only the longest row (the lengths stay on the
     device): rows whose lengths spread below it, timed with the heuristic's
     choice and with each forced number of workgroups per row."""
@@ -371,7 +371,7 @@ def sweep_spread(torch, ets, workloads, args, dev, cu, cap, steps) -> int:
                         os.environ["ETS_ROW_SPLIT"] = str(g)
                     w = Workload("spread-B%d-L%d-%s" % (B, L, spread), "raw", k, B, x, L=L,
                                  lens=lens, note="raw, N(0,1), lengths " + spread)
-                    rig = Rig(torch, ets, w, dev, cu, cap)
+                    rig = Rig(torch, ets, w, dev, limits)
                     us_g = timed(torch, rig.step, steps, args.warmup, False) * 1e3 / steps
                     if rig.ws is not None:
                         assert ets.workspace_error(rig.ws) == 0, "a bounded wait expired"
@@ -398,10 +398,10 @@ def sweep(torch, ets, workloads, args) -> int:
     from workloads import Workload
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cu, _, cap = ets.device_limits()
+    limits = ets.device_limits()
     steps = max(args.steps, 200)
     if args.sweep == "spread":
-        return sweep_spread(torch, ets, workloads, args, dev, cu, cap, steps)
+        return sweep_spread(torch, ets, workloads, args, dev, limits, steps)
     points = []
     if args.sweep == "batch":
         L, k, ps = 32768, 1024, 64
@@ -420,7 +420,7 @@ def sweep(torch, ets, workloads, args) -> int:
                                    lens=base.lens, page_table=base.page_table,
                                    page_size=base.page_size, note=base.note))
     for w in points:
-        rig = Rig(torch, ets, w, dev, cu, cap)
+        rig = Rig(torch, ets, w, dev, limits)
         us_g = timed(torch, rig.step, steps, args.warmup, False) * 1e3 / steps
         us_e = timed(torch, rig.step, steps, args.warmup, True) * 1e3 / steps
         ab = algorithmic_bytes(w)
@@ -484,7 +484,7 @@ class Rig:
     so the 256 MiB last-level cache cannot serve the scores), its output and
     workspace, and one step = one call on copy i % R."""
 
-    def __init__(self, torch, ets, w, dev, cu, cap):
+    def __init__(self, torch, ets, w, dev, limits):
         self.w, self.dev, self.torch, self.ets = w, dev, torch, ets
         per_copy = w.scores.nbytes
         self.R = R = max(1, -(-RING_BYTES // per_copy))
@@ -496,7 +496,7 @@ class Rig:
         self.max_len = w.max_len if w.api == "ragged" else w.L
         # one zero-filled workspace for every step (each call leaves it zero)
         self.ws = ws = ets.new_workspace(w.B, self.max_len, w.k, dev)
-        self.split = ets.row_split(w.B, self.max_len, cu, cap)
+        self.split = ets.row_split(w.B, self.max_len, *limits)
         self.kernel = ("group_topk_kernel (%d workgroups per row)" % self.split if self.split
                        else "row_topk_kernel")
         if w.api == "paged":

@@ -27,7 +27,7 @@ from typing import Optional
 import torch
 
 __all__ = ["topk_raw", "topk_paged", "topk_ragged", "topk_paged_noalloc", "workspace_size", "row_split", "floor_read",
-           "floor_launch", "device_limits", "group_cap",
+           "floor_launch", "device_limits", "group_cap", "ticket_cap",
            "new_workspace", "workspace_init", "workspace_error", "workspace_error_async",
            "library_path", "MAX_K", "NOALLOC_SCRATCH_BYTES", "ERROR_BITS", "EtsError"]
 
@@ -72,12 +72,13 @@ def _load():
             lib.ets_topk_paged_window.argtypes = [vp, i64, i32, i32, vp, vp, vp, i64, i32, i32, vp,
                                                   i64, vp, sz, vp]
             lib.ets_workspace_size.argtypes = [i32, i64, i32, i32, ctypes.POINTER(sz)]
-            lib.ets_row_split.argtypes = [i32, i64, i32, i32]
+            lib.ets_row_split.argtypes = [i32, i64, i32, i32, i32]
             lib.ets_workspace_init.argtypes = [vp, sz, vp]
             lib.ets_workspace_error.argtypes = [vp, sz, vp, vp]
             pi32 = ctypes.POINTER(i32)
             lib.ets_device_limits.argtypes = [i32, pi32, pi32, pi32]
             lib.ets_group_cap.argtypes = [i32, i32, i32]
+            lib.ets_ticket_cap.argtypes = [i32, i32, i32]
             lib.ets_status_string.argtypes = [i32]
             lib.ets_floor_read.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp, i64, vp]
             lib.ets_floor_launch.argtypes = [i32, i64, vp]
@@ -85,7 +86,7 @@ def _load():
                        lib.ets_topk_paged_noalloc, lib.ets_topk_paged_window,
                        lib.ets_workspace_size, lib.ets_row_split, lib.ets_workspace_init,
                        lib.ets_workspace_error, lib.ets_device_limits, lib.ets_group_cap,
-                       lib.ets_floor_read, lib.ets_floor_launch):
+                       lib.ets_ticket_cap, lib.ets_floor_read, lib.ets_floor_launch):
                 fn.restype = ctypes.c_int32
             lib.ets_status_string.restype = ctypes.c_char_p
             _lib = lib
@@ -176,11 +177,12 @@ def workspace_size(B: int, max_row_len: int, k: int, device: Optional[int] = Non
     return nbytes.value
 
 
-def row_split(B: int, max_row_len: int, cu_count: int, max_group: int) -> int:
-    """Workgroups per row chosen for (B, max_row_len) on a device with ``cu_count``
-    CUs whose largest row group is ``max_group`` (0 = one per row, -1 = an
-    ETS_ROW_SPLIT override above max_group, which the calls reject)."""
-    return int(_load().ets_row_split(B, max_row_len, cu_count, max_group))
+def row_split(B: int, max_row_len: int, cu_count: int, xcd_count: int, groups_per_cu: int) -> int:
+    """Workgroups per row chosen for (B, max_row_len) on a device of ``cu_count``
+    CUs in ``xcd_count`` XCDs, each CU holding ``groups_per_cu`` row-group
+    workgroups (0 = one per row, -1 = an ETS_ROW_SPLIT override above
+    group_cap, which the calls reject)."""
+    return int(_load().ets_row_split(B, max_row_len, cu_count, xcd_count, groups_per_cu))
 
 
 def group_cap(cu_count: int, xcd_count: int, groups_per_cu: int) -> int:
@@ -188,12 +190,19 @@ def group_cap(cu_count: int, xcd_count: int, groups_per_cu: int) -> int:
     return int(_load().ets_group_cap(cu_count, xcd_count, groups_per_cu))
 
 
+def ticket_cap(cu_count: int, xcd_count: int, groups_per_cu: int) -> int:
+    """Largest row group one launch of a grid that does not fit the device at
+    once takes: one shader engine's row-group slots (pure host function)."""
+    return int(_load().ets_ticket_cap(cu_count, xcd_count, groups_per_cu))
+
+
 def device_limits(device: Optional[int] = None):
-    """(compute units, XCDs, largest row group) of a device (default: current)."""
-    cu, xcd, cap = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    """(compute units, XCDs, row-group workgroups per compute unit) of a device
+    (default: current): the inputs of row_split, group_cap and ticket_cap."""
+    cu, xcd, occ = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
     _check(_load().ets_device_limits(-1 if device is None else int(device), ctypes.byref(cu),
-                                     ctypes.byref(xcd), ctypes.byref(cap)), "ets_device_limits")
-    return cu.value, xcd.value, cap.value
+                                     ctypes.byref(xcd), ctypes.byref(occ)), "ets_device_limits")
+    return cu.value, xcd.value, occ.value
 
 
 # Workspace word set non-zero by a call that stopped waiting for the other
@@ -461,8 +470,8 @@ def floor_read(scores: torch.Tensor, lens: Optional[torch.Tensor] = None,
             raise ValueError("ragged rows need max_len")
         L, stride = 0, 0
     with torch.cuda.device(dev):
-        cu, _, cap = device_limits()
-    words = B * max(1, row_split(B, max_len, cu, cap))
+        limits = device_limits()
+    words = B * max(1, row_split(B, max_len, *limits))
     if sink is None:
         sink = torch.empty(max(words, 1), dtype=torch.int32, device=dev)
     _require(sink, "sink", torch.int32, 1)

@@ -11,7 +11,8 @@
 //  * before the histogram, each lane's largest (or second largest) key is
 //    reduced to a provable lower bound of the k-th largest score: the lanes'
 //    maxima are k distinct scores, so at least k scores are >= their minimum.
-//    Scores below the bound never touch the LDS histogram;
+//    Scores below the bound count into per-lane dummy bins past the
+//    histogram, never into its bins;
 //  * the histogram range adapts to [bound, row max], so one 4096-bin round
 //    usually leaves a threshold bucket of a few scores;
 //  * ties are resolved on the 64-bit composite (key, ~position), which is
@@ -1245,22 +1246,29 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 //
 // Members are assigned by workgroup index, a row's G members on one XCD,
 // when the whole grid fits the device's row-group slots at once; otherwise
-// groups are formed in the order workgroups start (a ticket counter).  Why a ticketed grid always finishes
-// when G is at most the row-group slots of one XCD (its compute units times
-// the workgroups one compute unit holds; the host derives that cap from the
-// device): tickets are consecutive, so every group whose G tickets are all
-// taken has all of its members started, waits only for them and finishes;
-// only the group holding the newest ticket can be incomplete, with at most
-// G - 1 started members waiting.  The dispatcher deals workgroups to XCDs by
-// index, so near the end of the grid only one XCD may still be starting
-// them; the waiting members occupy at most G - 1 of its slots, so a slot
-// frees up as the complete groups finish, the next workgroup starts and takes
-// the next ticket.  With G above one XCD's slots the incomplete group can
-// hold every slot of the last XCD while its missing members are queued
-// behind them there: a wait then runs to its bound.  Every wait is bounded;
-// on expiry the workspace's error word gets the bit of that wait (bounds
-// exchange, coarse table or round barrier), the call's output is undefined,
-// and the kernel still ends.
+// groups are formed in the order workgroups start (a ticket counter), or the
+// batch is cut into several such index grids.  How workgroups reach the
+// compute units (measured on MI355X): workgroup i goes to XCD i % 8, and each
+// XCD deals its own workgroups, in order, to its 4 shader engines in a fixed
+// rotation, waiting for a slot on the engine whose turn it is even while the
+// other engines have free ones.  An index grid that fits the device is
+// resident at once: no engine is dealt more than ceil(grid / 32) <= 8 of it,
+// so no member ever waits for a workgroup that has not started.  Why a
+// ticketed grid always finishes when G is at most one engine's row-group
+// slots (its compute units times the workgroups one compute unit holds; the
+// host derives that cap from the device): tickets are consecutive, so every
+// group whose G tickets are all taken has all of its members started, waits
+// only for them and finishes; only the group holding the newest ticket can be
+// incomplete, with at most G - 1 started members waiting.  They cannot fill
+// an engine, so on every XCD the engine whose turn it is holds a member of a
+// complete group or a free slot, and that XCD goes on starting workgroups,
+// which take the next tickets.  With G above one engine's slots the
+// incomplete group can fill the engine whose turn it is on the only XCD still
+// starting workgroups, its missing members queued behind it there: a wait
+// then runs to its bound (seen at G = 32 and 64 on grids of thousands of
+// workgroups).  Every wait is bounded; on expiry the workspace's error word
+// gets the bit of that wait (bounds exchange, coarse table or round barrier),
+// the call's output is undefined, and the kernel still ends.
 
 // Data crosses workgroups only through agent-scope relaxed atomics, with each
 // wave's memory counter drained before an arrival is counted (or, for the
@@ -1336,9 +1344,6 @@ __device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
 template <class U>
 __device__ __forceinline__ U add_dev(U* p, U v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void max_dev(uint32_t* p, uint32_t v) {
-  __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void or_dev(uint32_t* p, uint32_t v) {
   __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1922,23 +1927,22 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   }
 }
 
-// One launch for the whole batch, G workgroups per row.  TICKET: B * G
-// workgroups take rows in the order they start (a device counter), so that
-// a group only waits for members that have started or start next and
-// progress needs room for one group on one XCD (G at most one XCD's
-// row-group slots, checked by the host).  Otherwise members are assigned by
-// workgroup index: the dispatcher deals workgroup i to XCD i % nx, and the
-// grid (nx * G * ceil(B / nx) workgroups, the padding idle) gives each row
-// the G workgroups of one XCD, so that its exchanges wait only for that
-// XCD's starts (XCDs start a launch up to 2 us apart; on MI355X, C5 13.4 us
-// against 14.1 with rows spread over every XCD).  The placement only affects
-// speed.  The host chooses this only when the whole grid fits the device's
-// row-group slots at once, where waiting members can never keep the rest of
-// the grid from starting, wherever they run (work of other streams that
-// holds compute units only delays them, until it ends).
+// G workgroups per row.  TICKET: B * G workgroups take rows in the order
+// they start (a device counter), so that a group only waits for members that
+// have started or start next; progress needs G within one shader engine's
+// row-group slots (checked by the host).  Otherwise members are assigned by
+// workgroup index over rows [b0, B): the dispatcher deals workgroup i to XCD
+// i % nx, and the grid (nx * G * ceil((B - b0) / nx) workgroups, the padding
+// idle) gives each row the G workgroups of one XCD, so that its exchanges
+// wait only for that XCD's starts (XCDs start a launch up to 2 us apart; on
+// MI355X, C5 13.4 us against 14.1 with rows spread over every XCD).  The
+// placement only affects speed.  The host launches such a grid only when it
+// fits the device's row-group slots at once, where waiting members can never
+// keep the rest of the grid from starting, wherever they run (work of other
+// streams that holds compute units only delays them, until it ends).
 template <int T, int VEC, int MODE, bool V4, bool TICKET>
 __global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, int32_t B, int32_t G,
-                                                       int32_t nx) {
+                                                       int32_t nx, int32_t b0) {
   __shared__ GroupSmem sm;
   const GroupWs w(ws);
   int b, g;
@@ -1951,7 +1955,7 @@ __global__ __launch_bounds__(T) void group_topk_kernel(Params p, uint32_t* ws, i
     // workgroup i starts on XCD i % nx: row b's members are the workgroups
     // of XCD b % nx, so that a row's exchanges wait for one XCD's starts only
     const uint32_t x = blockIdx.x % static_cast<uint32_t>(nx), s = blockIdx.x / static_cast<uint32_t>(nx);
-    b = static_cast<int>(x + static_cast<uint32_t>(nx) * (s / static_cast<uint32_t>(G)));
+    b = b0 + static_cast<int>(x + static_cast<uint32_t>(nx) * (s / static_cast<uint32_t>(G)));
     g = static_cast<int>(s % static_cast<uint32_t>(G));
     if (b >= B) return;  // the grid's padding
   }
@@ -2072,6 +2076,7 @@ struct DeviceInfo {
   int xcd_count = 0;   // XCDs (dies with their own L2 and workgroup dispatcher)
   int group_occ = 0;   // row-group workgroups one compute unit holds at once
   int group_cap = 0;   // largest row group whose members fit the slots of one XCD
+  int ticket_cap = 0;  // largest row group a ticketed grid takes: one shader engine's slots
 };
 
 constexpr int kMaxDevices = 64;
@@ -2091,6 +2096,26 @@ int32_t group_cap_of(int32_t cu_count, int32_t xcd_count, int32_t per_cu) {
   if (cu_count <= 0 || xcd_count <= 0 || per_cu <= 0) return 0;
   const int64_t slots = static_cast<int64_t>(cu_count / xcd_count) * per_cu;
   return static_cast<int32_t>(std::min<int64_t>(slots, kGroupSlotCap));
+}
+
+// Shader engines per XCD on gfx950.  Each XCD deals its workgroups to its
+// engines in a fixed rotation and waits, in order, for a slot on the engine
+// whose turn it is (measured on MI355X: workgroups that held one engine's
+// compute units 40 times longer than the others still received exactly a
+// quarter of each XCD's workgroups, and the rest of the XCD waited for them).
+constexpr int kEnginesPerXcd = 4;
+
+// The largest row group a ticketed grid may take.  Its waiting members (at
+// most G - 1, all in the group holding the newest ticket) must leave a slot
+// on every engine, or the engine whose turn it is can hold only waiting
+// members and its XCD stops starting workgroups; near the end of the grid
+// no other XCD may be left to start the group's missing members.  So G is at
+// most one engine's row-group slots: its compute units times the workgroups
+// one compute unit holds (8 on MI355X).
+int32_t ticket_cap_of(int32_t cu_count, int32_t xcd_count, int32_t per_cu) {
+  if (cu_count <= 0 || xcd_count <= 0 || per_cu <= 0) return 0;
+  const int64_t slots = static_cast<int64_t>(cu_count / xcd_count / kEnginesPerXcd) * per_cu;
+  return static_cast<int32_t>(std::min<int64_t>(std::max<int64_t>(slots, 1), kGroupSlotCap));
 }
 
 ets_status device_info(int dev, DeviceInfo* info_out) {
@@ -2115,6 +2140,7 @@ ets_status device_info(int dev, DeviceInfo* info_out) {
       if (cur != dev) (void)hipSetDevice(cur);
       if (d.group_occ <= 0) return ETS_ERR_DEVICE;
       d.group_cap = group_cap_of(d.cu_count, d.xcd_count, d.group_occ);
+      d.ticket_cap = ticket_cap_of(d.cu_count, d.xcd_count, d.group_occ);
     }
     d.queried = true;
   }
@@ -2188,10 +2214,14 @@ int group_kernel_occupancy() {
 // at G = 8), and one workgroup per row ahead once B reaches the CU count (the
 // rows alone then keep every compute unit busy) and where more than half the
 // compute units hold a row of at most two tiles (B = 192, L = 65536: 45.7 us
-// one per row, 48.7 at G = 2).  cu_count <= 0 (unknown) lifts the grid
-// bounds; max_group <= 0 (unknown) leaves the workspace's slot count as the
-// only cap.  ETS_ROW_SPLIT overrides: 0 or 1 = one workgroup per row, n >= 2
-// = n workgroups per row, n <= max_group.
+// one per row, 48.7 at G = 2).  The device is given by its compute units,
+// XCDs and the row-group workgroups one compute unit holds: G is at most one
+// XCD's slots (group_cap_of), and a grid beyond the device's slots keeps G
+// within one shader engine's slots (ticket_cap_of) where chunks of that many
+// members still fit one tile.  cu_count <= 0 (unknown) lifts the grid
+// bounds; an unknown XCD count or occupancy (<= 0) leaves the workspace's
+// slot count as the only cap.  ETS_ROW_SPLIT overrides: 0 or 1 = one
+// workgroup per row, n >= 2 = n workgroups per row, n at most the cap.
 // Fewest scores per member chunk of a split row: ets::kMinChunk, or the
 // environment variable ETS_MIN_CHUNK (read at every call) when it is an
 // integer >= 1, rounded up to a multiple of 4 and capped at one 32768-score
@@ -2208,9 +2238,10 @@ int32_t min_chunk_setting() {
   return ets::kMinChunk;
 }
 
-int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count, int32_t max_group) {
+int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count, int32_t xcd_count, int32_t per_cu) {
   if (B <= 0 || max_len <= 0) return 0;
-  const int64_t cap = max_group > 0 ? std::min<int64_t>(max_group, kGroupSlotCap) : kGroupSlotCap;
+  const bool known = cu_count > 0 && xcd_count > 0 && per_cu > 0;
+  const int64_t cap = known ? std::max(group_cap_of(cu_count, xcd_count, per_cu), 1) : kGroupSlotCap;
   if (const char* e = std::getenv("ETS_ROW_SPLIT"); e != nullptr && *e != '\0') {
     char* end = nullptr;
     const long v = std::strtol(e, &end, 10);
@@ -2228,7 +2259,21 @@ int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count, int32_t max_gro
     const int64_t resident = (max_len + kRowTile - 1) / kRowTile;  // fewest members whose chunks fit one tile
     G = std::min(G, std::max(fit, resident));
   }
-  return static_cast<int32_t>(G);
+  if (known) {
+    // A grid beyond the device's slots takes tickets only up to one shader
+    // engine's slots; above that it runs as several index grids (see
+    // launch_group).  Measured on MI355X, raw rows, k = 2048: the index grids
+    // cost more than a ticketed grid whose chunks still fit one tile (B = 20
+    // and 32, L = 262144: 28.5 and 31.0 us at G = 16 against 16.9 and 19.4 at
+    // G = 8), but less than a ticketed grid of streamed chunks (B = 16,
+    // L = 600000: 38.3 us at G = 32 against 78.3 at G = 8).
+    const int64_t slots = static_cast<int64_t>(cu_count) * per_cu;
+    const int64_t padded = static_cast<int64_t>(xcd_count) * G * ((B + xcd_count - 1) / xcd_count);
+    const int64_t tcap = ticket_cap_of(cu_count, xcd_count, per_cu);
+    const int64_t resident = (max_len + kRowTile - 1) / kRowTile;
+    if (padded > slots && G > tcap && resident <= tcap) G = tcap;
+  }
+  return G >= 2 ? static_cast<int32_t>(G) : 0;
 }
 
 size_t group_ws_bytes(int32_t B) {
@@ -2240,7 +2285,7 @@ size_t group_ws_bytes(int32_t B) {
 // workspace, before anything is enqueued.
 ets_status check_workspace(int32_t B, int64_t max_len, const DeviceInfo& info, const void* ws,
                            size_t ws_bytes) {
-  const int32_t G = split_plan(B, max_len, info.cu_count, info.group_cap);
+  const int32_t G = split_plan(B, max_len, info.cu_count, info.xcd_count, info.group_occ);
   if (G < 0) return ETS_ERR_INVALID_ARG;
   if (G == 0) return ETS_OK;
   if (static_cast<int64_t>(B) * G > INT32_MAX) return ETS_ERR_INVALID_ARG;
@@ -2254,25 +2299,36 @@ void launch_rows(const ets::Params& p, int32_t B, hipStream_t stream) {
                      p);
 }
 
-// Members are assigned by workgroup index, one XCD per row, only when the
-// whole padded grid fits the device's row-group slots at once (each compute
-// unit holds group_occ of them); otherwise by ticket in start order (see
-// group_topk_kernel).
+// Members are assigned by workgroup index, one XCD per row, when the whole
+// padded grid fits the device's row-group slots at once (each compute unit
+// holds group_occ of them); otherwise by ticket in start order (see
+// group_topk_kernel) when G is within ticket_cap; otherwise in several index
+// grids on the stream, each over as many whole rows per XCD as fit the
+// device at once.
 template <int MODE, bool V4, int VEC>
 void launch_group(const ets::Params& p, int32_t B, int32_t G, const DeviceInfo& info, void* ws,
                   hipStream_t stream) {
-  const uint32_t grid = static_cast<uint32_t>(B) * static_cast<uint32_t>(G);
   const int64_t slots = static_cast<int64_t>(info.cu_count) * info.group_occ;
   const int32_t nx = std::max(info.xcd_count, 1);
-  // by index: nx * G workgroups per nx rows, padded to whole rows per XCD
-  const int64_t padded = static_cast<int64_t>(nx) * G * ((B + nx - 1) / nx);
-  if (padded <= slots) {
+  auto index_grid = [&](int32_t b0, int32_t rows) {
+    // nx * G workgroups per nx rows, padded to whole rows per XCD
+    const int64_t padded = static_cast<int64_t>(nx) * G * ((rows + nx - 1) / nx);
     hipLaunchKernelGGL((ets::group_topk_kernel<kGroupThreads, VEC, MODE, V4, false>),
                        dim3(static_cast<uint32_t>(padded)), dim3(kGroupThreads), 0, stream, p,
-                       static_cast<uint32_t*>(ws), B, G, nx);
-  } else {
+                       static_cast<uint32_t*>(ws), b0 + rows, G, nx, b0);
+  };
+  const int64_t padded = static_cast<int64_t>(nx) * G * ((B + nx - 1) / nx);
+  if (padded <= slots) {
+    index_grid(0, B);
+  } else if (G <= info.ticket_cap) {
+    const uint32_t grid = static_cast<uint32_t>(B) * static_cast<uint32_t>(G);
     hipLaunchKernelGGL((ets::group_topk_kernel<kGroupThreads, VEC, MODE, V4, true>), dim3(grid),
-                       dim3(kGroupThreads), 0, stream, p, static_cast<uint32_t*>(ws), B, G, nx);
+                       dim3(kGroupThreads), 0, stream, p, static_cast<uint32_t*>(ws), B, G, nx, 0);
+  } else {
+    // G <= group_cap, so at least one row per XCD fits
+    const int32_t per_xcd = static_cast<int32_t>(std::max<int64_t>(1, slots / nx / G));
+    const int32_t rows = nx * per_xcd;
+    for (int32_t b0 = 0; b0 < B; b0 += rows) index_grid(b0, std::min(rows, B - b0));
   }
 }
 
@@ -2288,7 +2344,7 @@ struct Shape {
 };
 
 Shape launch_shape(int32_t B, int64_t max_len, const DeviceInfo& info) {
-  const int32_t G = split_plan(B, max_len, info.cu_count, info.group_cap);
+  const int32_t G = split_plan(B, max_len, info.cu_count, info.xcd_count, info.group_occ);
   if (G <= 0) {
     if (max_len <= 2048) return {1, 512, 1, false};
     if (max_len <= 4096) return {1, kRowThreads, 1, false};
@@ -2404,7 +2460,7 @@ ets_status ets_floor_read(const float* scores, int64_t row_stride, int32_t B, in
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
   const int64_t max_len = ragged ? max_len_hint : L;
-  if (split_plan(B, max_len, info.cu_count, info.group_cap) < 0) return ETS_ERR_INVALID_ARG;
+  if (split_plan(B, max_len, info.cu_count, info.xcd_count, info.group_occ) < 0) return ETS_ERR_INVALID_ARG;
   const Shape sh = launch_shape(B, max_len, info);
   const int64_t grid = static_cast<int64_t>(B) * sh.groups;
   if (grid > INT32_MAX || sink_words < grid) return ETS_ERR_INVALID_ARG;
@@ -2433,7 +2489,7 @@ ets_status ets_floor_launch(int32_t B, int64_t max_row_len, void* stream) {
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
-  if (split_plan(B, max_row_len, info.cu_count, info.group_cap) < 0) return ETS_ERR_INVALID_ARG;
+  if (split_plan(B, max_row_len, info.cu_count, info.xcd_count, info.group_occ) < 0) return ETS_ERR_INVALID_ARG;
   const Shape sh = launch_shape(B, max_row_len, info);
   const int64_t grid = static_cast<int64_t>(B) * sh.groups;
   if (grid > INT32_MAX) return ETS_ERR_INVALID_ARG;
@@ -2459,8 +2515,9 @@ const char* ets_status_string(ets_status status) {
   }
 }
 
-int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count, int32_t max_group) {
-  return split_plan(B, max_row_len, cu_count, max_group);
+int32_t ets_row_split(int32_t B, int64_t max_row_len, int32_t cu_count, int32_t xcd_count,
+                      int32_t groups_per_cu) {
+  return split_plan(B, max_row_len, cu_count, xcd_count, groups_per_cu);
 }
 
 ets_status ets_workspace_size(int32_t B, int64_t max_row_len, int32_t k, int32_t device,
@@ -2471,7 +2528,7 @@ ets_status ets_workspace_size(int32_t B, int64_t max_row_len, int32_t k, int32_t
   int dev = device;
   if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return ETS_ERR_DEVICE;
   if (ets_status st = device_info(dev, &info); st != ETS_OK) return st;
-  const int32_t G = split_plan(B, max_row_len, info.cu_count, info.group_cap);
+  const int32_t G = split_plan(B, max_row_len, info.cu_count, info.xcd_count, info.group_occ);
   if (G < 0) return ETS_ERR_INVALID_ARG;
   *bytes = (G == 0 || B == 0) ? 0 : group_ws_bytes(B);
   return ETS_OK;
@@ -2498,20 +2555,24 @@ ets_status ets_workspace_error(void* workspace, size_t workspace_bytes, int32_t*
 }
 
 ets_status ets_device_limits(int32_t device, int32_t* cu_count, int32_t* xcd_count,
-                             int32_t* group_cap) {
-  if (!cu_count || !xcd_count || !group_cap) return ETS_ERR_INVALID_ARG;
+                             int32_t* groups_per_cu) {
+  if (!cu_count || !xcd_count || !groups_per_cu) return ETS_ERR_INVALID_ARG;
   int dev = device;
   if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return ETS_ERR_DEVICE;
   DeviceInfo info;
   if (ets_status st = device_info(dev, &info); st != ETS_OK) return st;
   *cu_count = info.cu_count;
   *xcd_count = info.xcd_count;
-  *group_cap = info.group_cap;
+  *groups_per_cu = info.group_occ;
   return ETS_OK;
 }
 
 int32_t ets_group_cap(int32_t cu_count, int32_t xcd_count, int32_t groups_per_cu) {
   return group_cap_of(cu_count, xcd_count, groups_per_cu);
+}
+
+int32_t ets_ticket_cap(int32_t cu_count, int32_t xcd_count, int32_t groups_per_cu) {
+  return ticket_cap_of(cu_count, xcd_count, groups_per_cu);
 }
 
 ets_status ets_topk_raw(const float* scores, int64_t row_stride, int32_t B, int32_t L,
@@ -2620,7 +2681,7 @@ ets_status ets_topk_paged_noalloc(const float* scores, int64_t row_stride, int32
   int dev;
   DeviceInfo info;
   if (ets_status st = current_device(&dev, &info); st != ETS_OK) return st;
-  const int32_t G = split_plan(B, L, info.cu_count, info.group_cap);
+  const int32_t G = split_plan(B, L, info.cu_count, info.xcd_count, info.group_occ);
   if (G < 0 || static_cast<int64_t>(B) * G > INT32_MAX) return ETS_ERR_INVALID_ARG;
   const size_t need = G == 0 ? 0 : group_ws_bytes(B);
   if (need > ets::kScratchBytes) return ETS_ERR_SCRATCH;

@@ -80,23 +80,25 @@ int main(void) {
   EXPECT(ets_group_cap(256, 8, 1), 32);
   EXPECT(ets_group_cap(304, 8, 3), 64);
   EXPECT(ets_group_cap(0, 8, 1), 0);
+  EXPECT(ets_ticket_cap(256, 8, 1), 8);
+  EXPECT(ets_ticket_cap(0, 8, 1), 0);
   (void)a;
   unsetenv("ETS_ROW_SPLIT");
-  EXPECT(ets_row_split(4, 262144, 256, 32), 16);
-  EXPECT(ets_row_split(64, 32768, 256, 32), 0);
-  EXPECT(ets_row_split(192, 65536, 256, 32), 0);
-  EXPECT(ets_row_split(1, (int64_t)1 << 40, 256, 0), 64);
-  EXPECT(ets_row_split(2147483647, (int64_t)1 << 40, 256, 32), 0);
+  EXPECT(ets_row_split(4, 262144, 256, 8, 1), 16);
+  EXPECT(ets_row_split(64, 32768, 256, 8, 1), 0);
+  EXPECT(ets_row_split(192, 65536, 256, 8, 1), 0);
+  EXPECT(ets_row_split(1, (int64_t)1 << 40, 256, 0, 1), 64);
+  EXPECT(ets_row_split(2147483647, (int64_t)1 << 40, 256, 8, 1), 0);
   setenv("ETS_ROW_SPLIT", "7", 1);
-  EXPECT(ets_row_split(4, 262144, 256, 32), 7);
+  EXPECT(ets_row_split(4, 262144, 256, 8, 1), 7);
   setenv("ETS_ROW_SPLIT", "33", 1);
-  EXPECT(ets_row_split(4, 262144, 256, 32), -1);
+  EXPECT(ets_row_split(4, 262144, 256, 8, 1), -1);
   setenv("ETS_ROW_SPLIT", "99999999999999999999", 1);
-  EXPECT(ets_row_split(4, 262144, 256, 32), -1);
+  EXPECT(ets_row_split(4, 262144, 256, 8, 1), -1);
   setenv("ETS_ROW_SPLIT", "-3", 1);  /* not an override: the heuristic applies */
-  EXPECT(ets_row_split(4, 262144, 256, 32), 16);
+  EXPECT(ets_row_split(4, 262144, 256, 8, 1), 16);
   setenv("ETS_ROW_SPLIT", "4x", 1);
-  EXPECT(ets_row_split(4, 262144, 256, 32), 16);
+  EXPECT(ets_row_split(4, 262144, 256, 8, 1), 16);
   unsetenv("ETS_ROW_SPLIT");
   for (int s = -1; s <= 7; ++s) {
     const char* t = ets_status_string(s);

@@ -136,10 +136,25 @@ def test_group_cap():
     assert ets.group_cap(0, 8, 1) == 0 and ets.group_cap(256, 0, 1) == 0 and ets.group_cap(256, 8, 0) == 0
 
 
+def test_ticket_cap():
+    """One shader engine's row-group slots: an XCD's compute units over its 4
+    engines, times the row-group workgroups each holds, at least 1 and at
+    most 64."""
+    import exact_top_selection_amd as ets
+    assert ets.ticket_cap(256, 8, 1) == 8   # MI355X: 8 CUs per engine, one 1024-lane workgroup each
+    assert ets.ticket_cap(256, 8, 2) == 16
+    assert ets.ticket_cap(32, 1, 1) == 8    # one XCD as its own device
+    assert ets.ticket_cap(256, 8, 16) == 64
+    assert ets.ticket_cap(8, 8, 1) == 1
+    assert ets.ticket_cap(0, 8, 1) == 0 and ets.ticket_cap(256, 0, 1) == 0 and ets.ticket_cap(256, 8, 0) == 0
+    for cu, x, occ in ((256, 8, 1), (304, 8, 1), (256, 8, 2), (80, 1, 1)):
+        assert ets.ticket_cap(cu, x, occ) <= ets.group_cap(cu, x, occ)
+
+
 def test_row_split_env_override(tmp_path):
     code = ("import exact_top_selection_amd as e; "
-            "print(e.row_split(4, 262144, 256, 32), e.row_split(64, 32768, 256, 32), "
-            "e.row_split(4, 262144, 256, 64))")
+            "print(e.row_split(4, 262144, 256, 8, 1), e.row_split(64, 32768, 256, 8, 1), "
+            "e.row_split(4, 262144, 256, 8, 2))")
 
     def run(v):
         env = dict(os.environ, ETS_ROW_SPLIT=v, PYTHONPATH=ROOT)
@@ -161,59 +176,76 @@ def test_row_split_heuristic():
     try:
         # rows that fit one 32768-score workgroup tile stay whole, whatever the batch
         for B, L in ((64, 32768), (128, 32768), (48, 8192), (1, 2048), (4, 4096), (1024, 8192)):
-            assert ets.row_split(B, L, 256, 32) == 0, (B, L)
+            assert ets.row_split(B, L, 256, 8, 1) == 0, (B, L)
         # longer rows are cut into chunks of about 16384 scores, at most 32
-        assert ets.row_split(4, 32769, 256, 32) == 3
-        assert ets.row_split(4, 65536, 256, 32) == 4
-        assert ets.row_split(2, 100000, 256, 32) == 7
-        assert ets.row_split(4, 262144, 256, 32) == 16
-        assert ets.row_split(16, 262144, 256, 32) == 16
-        assert ets.row_split(1, 10 ** 7, 256, 32) == 32
-        assert ets.row_split(0, 262144, 256, 32) == 0
+        assert ets.row_split(4, 32769, 256, 8, 1) == 3
+        assert ets.row_split(4, 65536, 256, 8, 1) == 4
+        assert ets.row_split(2, 100000, 256, 8, 1) == 7
+        assert ets.row_split(4, 262144, 256, 8, 1) == 16
+        assert ets.row_split(16, 262144, 256, 8, 1) == 16
+        assert ets.row_split(1, 10 ** 7, 256, 8, 1) == 32
+        assert ets.row_split(0, 262144, 256, 8, 1) == 0
         # the grid is held to two workgroups per compute unit ...
-        assert ets.row_split(64, 262144, 256, 32) == 8
-        assert ets.row_split(64, 65536, 256, 32) == 4
-        assert ets.row_split(128, 131072, 256, 32) == 4
+        assert ets.row_split(64, 262144, 256, 8, 1) == 8
+        assert ets.row_split(64, 65536, 256, 8, 1) == 4
+        assert ets.row_split(128, 131072, 256, 8, 1) == 4
         # ... unless that leaves chunks longer than one 32768-score tile ...
-        assert ets.row_split(128, 262144, 256, 32) == 8
-        assert ets.row_split(192, 131072, 256, 32) == 4
+        assert ets.row_split(128, 262144, 256, 8, 1) == 8
+        assert ets.row_split(192, 131072, 256, 8, 1) == 4
         # ... but rows of at most two tiles stay whole once B > CUs / 2
-        assert ets.row_split(192, 65536, 256, 32) == 0
-        assert ets.row_split(128, 65536, 256, 32) == 4
-        assert ets.row_split(64, 10 ** 7, 256, 32) == 32
+        assert ets.row_split(192, 65536, 256, 8, 1) == 0
+        assert ets.row_split(128, 65536, 256, 8, 1) == 4
+        assert ets.row_split(64, 10 ** 7, 256, 8, 1) == 32
         # ... and rows stay whole once the batch alone fills the device
-        assert ets.row_split(256, 65536, 256, 32) == 0
-        assert ets.row_split(4096, 262144, 256, 32) == 0
+        assert ets.row_split(256, 65536, 256, 8, 1) == 0
+        assert ets.row_split(4096, 262144, 256, 8, 1) == 0
         # an unknown compute-unit count lifts the bound
-        assert ets.row_split(4, 262144, 0, 32) == 16
-        assert ets.row_split(4096, 262144, 0, 32) == 16
-        # the device's group cap bounds G; an unknown cap leaves the 64 record slots
-        assert ets.row_split(1, 10 ** 7, 256, 20) == 20
-        assert ets.row_split(1, 10 ** 7, 256, 0) == 64
-        assert ets.row_split(1, 10 ** 7, 256, 100) == 64
+        assert ets.row_split(4, 262144, 0, 8, 1) == 16
+        assert ets.row_split(4096, 262144, 0, 8, 1) == 16
+        # the device's group cap bounds G (one XCD's slots: 20 for 160 CUs in 8
+        # XCDs); an unknown XCD count or occupancy leaves the 64 record slots
+        assert ets.row_split(1, 10 ** 7, 160, 8, 1) == 20
+        assert ets.row_split(1, 10 ** 7, 256, 0, 1) == 64
+        assert ets.row_split(1, 10 ** 7, 256, 8, 0) == 64
+        assert ets.row_split(1, 10 ** 7, 256, 8, 4) == 64
+        # a grid beyond the device's slots keeps G within one shader engine's
+        # slots (8) where chunks of 8 members still fit one tile ...
+        assert ets.row_split(20, 262144, 256, 8, 1) == 8
+        assert ets.row_split(32, 262144, 256, 8, 1) == 8
+        assert ets.row_split(48, 200000, 256, 8, 1) == 8
+        assert ets.row_split(16, 262144, 256, 8, 1) == 16  # 256 workgroups: fits
+        assert ets.row_split(20, 262144, 256, 8, 2) == 16  # two per CU: 384 of 512 slots
+        # ... and keeps the heuristic's G where they would not (several index grids)
+        assert ets.row_split(16, 600000, 256, 8, 1) == 32
     finally:
         if env is not None:
             os.environ["ETS_ROW_SPLIT"] = env
 
 
 def test_row_split_bounds_hold_everywhere():
-    """Over a grid of shapes: at most 32 workgroups per row, never a split of a
-    row that fits one 32768-score tile or of a batch that fills the device,
-    and the grid within two workgroups per compute unit unless chunks would
-    outgrow one tile."""
+    """Over a grid of shapes and devices: at most one XCD's row-group slots per
+    row, never a split of a row that fits one 32768-score tile or of a batch
+    that fills the device, the grid within two workgroups per compute unit
+    unless chunks would outgrow one tile, and a grid beyond the device's slots
+    above one shader engine's slots only where chunks that many members would
+    give outgrow one tile."""
     import exact_top_selection_amd as ets
     env = os.environ.pop("ETS_ROW_SPLIT", None)
     try:
-        for cu in (80, 256, 304):
+        for cu, nx in ((80, 1), (256, 8), (304, 8)):
+            cap, tcap = ets.group_cap(cu, nx, 1), ets.ticket_cap(cu, nx, 1)
             for B in (1, 2, 3, 5, 8, 17, 64, 100, 128, 129, 256, 1000):
                 for L in (1, 32768, 32769, 65536, 100000, 262144, 10 ** 6, 2 ** 31 - 1):
-                    g = ets.row_split(B, L, cu, 32)
-                    assert 0 <= g <= 32, (cu, B, L, g)
+                    g = ets.row_split(B, L, cu, nx, 1)
+                    assert 0 <= g <= cap, (cu, B, L, g)
                     if L <= 32768 or B >= cu:
                         assert g == 0, (cu, B, L, g)
                     if g:
                         tiles = -(-L // 32768)
                         assert g >= 2 and B * g <= max(2 * cu, B * tiles), (cu, B, L, g)
+                        padded = nx * g * -(-B // nx)
+                        if padded > cu and g > tcap:
+                            assert tiles > tcap, (cu, B, L, g)
     finally:
         if env is not None:
             os.environ["ETS_ROW_SPLIT"] = env

@@ -34,15 +34,15 @@ def _expected(rows, G):
 def test_floor_read_reports_each_span_max(name):
     w = workloads.make(name, seed=7)
     d = dev()
-    cu, _, cap = ets.device_limits()
+    limits = ets.device_limits()
     if w.api == "ragged":
-        G = max(1, ets.row_split(w.B, w.max_len, cu, cap))
+        G = max(1, ets.row_split(w.B, w.max_len, *limits))
         s = torch.from_numpy(w.scores).to(d)
         got = ets.floor_read(s, torch.from_numpy(w.lengths).to(d),
                              torch.from_numpy(w.row_starts).to(d), w.max_len)
         rows = [w.scores[a:a + n] for a, n in zip(w.row_starts, w.lengths)]
     else:
-        G = max(1, ets.row_split(w.B, w.L, cu, cap))
+        G = max(1, ets.row_split(w.B, w.L, *limits))
         lens = None if w.lens is None else torch.from_numpy(w.lens).to(d)
         got = ets.floor_read(torch.from_numpy(w.scores).to(d), lens)
         n = w.lens if w.lens is not None else np.full(w.B, w.L)

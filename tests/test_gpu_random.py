@@ -153,7 +153,7 @@ def _oracle(w, wins):
 def run_case(seed):
     """Runs one random case on the GPU and checks it against the oracle."""
     w, env, wins = random_case(seed)
-    cu, _, cap = ets.device_limits()
+    cap = ets.group_cap(*ets.device_limits())
     if "ETS_ROW_SPLIT" in env and int(env["ETS_ROW_SPLIT"]) > cap:
         env["ETS_ROW_SPLIT"] = str(cap)
     print("case", w.name, env, "noalloc" if w.extra.get("noalloc") else "", flush=True)

@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import exact_top_selection_amd as ets
+import oracle
 import workloads
 from workloads import Workload
 from tests.gpu_helpers import WS_HDR, WS_ROW, assert_parity, dev, run_gpu, run_oracle, workspace_dirty
@@ -366,10 +367,11 @@ def test_workspace_size_formula():
 
 
 def test_large_row_group_grids():
-    """Grids of 2048 workgroups (64 rows of 32 members, start-order tickets)
-    and rows of over a million scores on the default split: every bounded
-    wait ends in time (error word zero) over repeated calls, and the output
-    matches the oracle."""
+    """64 rows of 32 members (2048 workgroups, more than the device holds at
+    once: eight index grids of 8 rows, since 32 members exceed one shader
+    engine's slots) and rows of over a million scores on the default split:
+    every bounded wait ends in time (error word zero) over repeated calls, and
+    the output matches the oracle."""
     d = dev()
     k = 2048
     for B, L, g in ((64, 131072, 32), (2, 1500000, None)):
@@ -386,6 +388,49 @@ def test_large_row_group_grids():
         w = _raw("large-grid", x, k)
         assert_parity(w, out.cpu().numpy(), run_oracle(w))
         _assert_clean(ws)
+
+
+@pytest.mark.parametrize("B,L,k,g,window", [
+    (134, 55023, 4, 32, True),    # the random call whose ticketed grid ran into a bounded wait
+    (64, 131072, 2048, 16, False),
+    (40, 262144, 1024, 9, False),
+    (70, 40000, 100, 12, True),
+])
+def test_groups_above_one_engine_on_grids_beyond_the_device(B, L, k, g, window):
+    """G above one shader engine's row-group slots on a batch whose grid does
+    not fit the device at once: the library runs it as several index grids
+    (as many whole rows per XCD as fit), never as a ticketed grid, and every
+    call matches the oracle with the error word zero and the workspace clean."""
+    d = dev()
+    cu, nx, occ = ets.device_limits()
+    assert ets.ticket_cap(cu, nx, occ) < g <= ets.group_cap(cu, nx, occ)
+    rng = np.random.default_rng(B * L + g)
+    x = rng.standard_normal((B, L)).astype(np.float32)
+    lens = rng.integers(L // 2, L + 1, size=B).astype(np.int32)
+    ps = 64
+    P = -(-L // ps)
+    pt = np.stack([rng.permutation(P) for _ in range(B)]).astype(np.int32)
+    wins = rng.integers(0, L // 4, size=B).astype(np.int32) if window else None
+    print("case B", B, "L", L, "k", k, "G", g, "window", window, flush=True)
+    with split(g):
+        ws = ets.new_workspace(B, L, k, d)
+        out = torch.full((B, k), -7, dtype=torch.int32, device=d)
+        for _ in range(2):
+            ets.topk_paged(torch.from_numpy(x).to(d), torch.from_numpy(lens).to(d), torch.from_numpy(pt).to(d),
+                           out, ps, workspace=ws,
+                           window_starts=None if wins is None else torch.from_numpy(wins).to(d))
+            _assert_clean(ws)
+    got = out.cpu().numpy()
+    n = np.clip(lens.astype(np.int64), 0, L)
+    lo = np.zeros(B, np.int64) if wins is None else np.clip(wins.astype(np.int64), 0, n)
+    starts = (np.arange(B) * L + lo).astype(np.int32)
+    flat = oracle.topk_ragged(np.ascontiguousarray(x.reshape(-1)), starts, (n - lo).astype(np.int32), k,
+                              threads=8)
+    want = np.full((B, k), -1, np.int32)
+    for b in range(B):
+        v = flat[b][flat[b] != -1].astype(np.int64) - b * L
+        want[b, :v.size] = pt[b, v // ps] * ps + v % ps
+    np.testing.assert_array_equal(np.sort(got, axis=1), np.sort(want, axis=1))
 
 
 def _banded(rng, B, L):
@@ -425,12 +470,13 @@ def test_banded_and_narrow_rows(kind, g):
 def test_split_override_above_cap_is_rejected():
     """ETS_ROW_SPLIT above the device's row-group cap is an argument error,
     reported before anything is enqueued, never a silent clamp."""
-    cu, xcd, cap = ets.device_limits()
-    assert cap == ets.group_cap(cu, xcd, 1) or cap >= 2
+    cu, xcd, occ = ets.device_limits()
+    cap = ets.group_cap(cu, xcd, occ)
+    assert cap >= 2
     d = dev()
     x = torch.zeros((2, 65536), dtype=torch.float32, device=d)
     with split(cap + 1):
-        assert ets.row_split(2, 65536, cu, cap) == -1
+        assert ets.row_split(2, 65536, cu, xcd, occ) == -1
         with pytest.raises(ets.EtsError) as e:
             ets.topk_raw(x, 64)
         assert e.value.status == 1
@@ -447,8 +493,8 @@ def test_default_heuristic_large_batches(B, L, k):
     """The heuristic's choices for long rows at large batches: chunks of 32768
     scores held in registers on a ticketed grid (B = 128, L = 262144: G = 8;
     B = 192, L = 131072: G = 4) and whole streamed rows (B = 192, L = 65536)."""
-    cu, _, cap = ets.device_limits()
-    print("case default B", B, "L", L, "G", ets.row_split(B, L, cu, cap), flush=True)
+    limits = ets.device_limits()
+    print("case default B", B, "L", L, "G", ets.row_split(B, L, *limits), flush=True)
     rng = np.random.Generator(np.random.PCG64(B * 7 + L))
     x = workloads.normal_dense(rng, B, L)
     lens = rng.integers(L // 2, L, size=B, endpoint=True).astype(np.int32)
@@ -523,10 +569,10 @@ def test_stale_ticket_sets_the_error_word():
     error word says so; the last one re-arms the counter, so the next call on
     the same workspace is exact again."""
     d = dev()
-    cu, _, cap = ets.device_limits()
+    limits = ets.device_limits()
     B, L, k = 64, 131072, 2048
-    G = ets.row_split(B, L, cu, cap)
-    assert G * B > cu, "needs a ticketed grid"
+    G = ets.row_split(B, L, *limits)
+    assert G * B > limits[0], "needs a ticketed grid"
     x = workloads.normal_dense(np.random.Generator(np.random.PCG64(3)), B, L)
     s = torch.from_numpy(x).to(d)
     ws = ets.new_workspace(B, L, k, d)

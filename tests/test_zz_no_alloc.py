@@ -61,10 +61,10 @@ def _same_sets(got, want):
 def test_noalloc_matches_the_workspace_call():
     lib = ets._load()
     d = torch.device("cuda:0")
-    cu, _, cap = ets.device_limits()
+    limits = ets.device_limits()
     cases = [_case(71, 8, 131072, 2048), _case(72, 3, 70000, 1024)]
     for w in cases:
-        G = ets.row_split(w.B, w.L, cu, cap)
+        G = ets.row_split(w.B, w.L, *limits)
         print("case noalloc B", w.B, "L", w.L, "G", G, flush=True)
         assert G > 0, "the case must use the scratch"
         assert ets.workspace_size(w.B, w.L, w.k) <= SCRATCH_BYTES
@@ -82,9 +82,9 @@ def test_noalloc_matches_the_workspace_call():
 def test_noalloc_rejects_shapes_beyond_the_scratch():
     lib = ets._load()
     d = torch.device("cuda:0")
-    cu, _, cap = ets.device_limits()
+    limits = ets.device_limits()
     B, L, k = 64, 262144, 2048
-    assert ets.row_split(B, L, cu, cap) > 0 and ets.workspace_size(B, L, k) > SCRATCH_BYTES
+    assert ets.row_split(B, L, *limits) > 0 and ets.workspace_size(B, L, k) > SCRATCH_BYTES
     x = torch.zeros((1,), dtype=torch.float32, device=d)  # never read: rejected first
     lens = torch.zeros((B,), dtype=torch.int32, device=d)
     out = torch.full((B, k), 9, dtype=torch.int32, device=d)
@@ -103,11 +103,11 @@ def test_noalloc_graph_replays_match_the_oracle():
     same stream (which leaves the scratch zero in between), all equal the
     oracle, with the error flag at zero."""
     d = torch.device("cuda:0")
-    cu, _, cap = ets.device_limits()
+    limits = ets.device_limits()
     w = _case(81, 4, 70000, 1024)
     other = _case(82, 3, 131072, 2048)
     for c in (w, other):
-        assert ets.row_split(c.B, c.L, cu, cap) > 0
+        assert ets.row_split(c.B, c.L, *limits) > 0
     want = run_oracle(w)
     want_other = run_oracle(other)
     s = torch.from_numpy(w.scores).to(d)
