@@ -72,6 +72,68 @@ def test_graph_replays_match_the_oracle():
         del tmp, tmp5
 
 
+def test_graph_replays_of_batches_beyond_the_device():
+    """Inside one captured graph: a batch whose grid exceeds the device with G
+    above one shader engine's slots (B = 40, G = 16: three index grids of 16,
+    16 and 8 rows) and a ticketed batch (B = 64, L = 131072: the default G =
+    8).  Every replay matches the oracle, with the error word zero and both
+    workspaces clean."""
+    import os
+    from workloads import Workload
+    d = torch.device("cuda:0")
+    rng = np.random.Generator(np.random.PCG64(60))
+    w1 = Workload("graph-grids", "raw", 1024, 40, workloads.normal_dense(rng, 40, 100000), L=100000)
+    w2 = Workload("graph-ticket", "raw", 2048, 64, workloads.normal_dense(rng, 64, 131072), L=131072)
+    cu, nx, occ = ets.device_limits()
+    assert ets.row_split(w2.B, w2.L, cu, nx, occ) == ets.ticket_cap(cu, nx, occ)
+    s1, s2 = torch.from_numpy(w1.scores).to(d), torch.from_numpy(w2.scores).to(d)
+    want1, want2 = run_oracle(w1), run_oracle(w2)
+    g1 = torch.full((w1.B, w1.k), -7, dtype=torch.int32, device=d)
+    g2 = torch.full((w2.B, w2.k), -7, dtype=torch.int32, device=d)
+    saved = os.environ.pop("ETS_ROW_SPLIT", None)
+    try:
+        os.environ["ETS_ROW_SPLIT"] = "16"
+        ws1 = ets.new_workspace(w1.B, w1.L, w1.k, d)
+        os.environ.pop("ETS_ROW_SPLIT")
+        ws2 = ets.new_workspace(w2.B, w2.L, w2.k, d)
+        assert ws1 is not None and ws2 is not None
+        f1 = torch.zeros(1, dtype=torch.int32, device=d)
+        f2 = torch.zeros(1, dtype=torch.int32, device=d)
+        graph = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                os.environ["ETS_ROW_SPLIT"] = "16"
+                ets.topk_raw(s1, w1.k, out=g1, workspace=ws1)
+                os.environ.pop("ETS_ROW_SPLIT")
+                ets.topk_raw(s2, w2.k, out=g2, workspace=ws2)
+                ets.workspace_error_async(ws1, f1)
+                ets.workspace_error_async(ws2, f2)
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("ETS_ROW_SPLIT", None)
+        if saved is not None:
+            os.environ["ETS_ROW_SPLIT"] = saved
+    for rep in range(3):
+        g1.fill_(-9)
+        g2.fill_(-9)
+        f1.fill_(-1)
+        f2.fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        print("replay", rep, flush=True)
+        assert f1.item() == 0 and f2.item() == 0, "replay %d: a row group stopped waiting" % rep
+        assert_parity(w1, g1.cpu().numpy(), want1)
+        assert_parity(w2, g2.cpu().numpy(), want2)
+        assert workspace_dirty(ws1) == 0 and workspace_dirty(ws2) == 0
+        # eager work between replays, on other data
+        tmp = ets.topk_raw(s2.flip(1).contiguous(), w2.k, workspace=ws2)
+        torch.cuda.synchronize()
+        del tmp
+
+
 def test_capture_refuses_an_implicit_workspace():
     """A call that needs a workspace must be given one while a graph is being
     captured: the shared implicit buffer may be replaced (and freed) later."""
