@@ -1266,9 +1266,13 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // incomplete group can fill the engine whose turn it is on the only XCD still
 // starting workgroups, its missing members queued behind it there: a wait
 // then runs to its bound (seen at G = 32 and 64 on grids of thousands of
-// workgroups).  Every wait is bounded; on expiry the workspace's error word
-// gets the bit of that wait (bounds exchange, coarse table or round barrier),
-// the call's output is undefined, and the kernel still ends.
+// workgroups).  Both arguments count on the device's row-group slots: other
+// work only delays a member's start, but two row-group launches running at
+// once on one device (on different streams) can each hold slots that the
+// other's missing members need.  Every wait is bounded; on expiry the
+// workspace's error word gets the bit of that wait (bounds exchange, coarse
+// table or round barrier), the call's output is undefined, and the kernel
+// still ends.
 
 // Data crosses workgroups only through agent-scope relaxed atomics, with each
 // wave's memory counter drained before an arrival is counted (or, for the
@@ -2088,10 +2092,10 @@ int group_kernel_occupancy();  // fewest resident workgroups per CU over the row
 // Slots in a row's workspace record: the most members a row group can have.
 constexpr int kGroupSlotCap = 64;
 
-// The largest row group that is sure to make progress: a group waits only for
-// its own members, and near the end of a ticketed grid only one XCD may still
-// be starting workgroups, so a group of G must fit the row-group slots of one
-// XCD (its compute units times the workgroups one compute unit holds).
+// The largest row group: an index grid places a row's G members on one XCD,
+// so G is at most the row-group slots of one XCD (its compute units times the
+// workgroups one compute unit holds).  Ticketed grids take the smaller cap
+// of ticket_cap_of.
 int32_t group_cap_of(int32_t cu_count, int32_t xcd_count, int32_t per_cu) {
   if (cu_count <= 0 || xcd_count <= 0 || per_cu <= 0) return 0;
   const int64_t slots = static_cast<int64_t>(cu_count / xcd_count) * per_cu;

@@ -47,7 +47,12 @@
  *     of calls, including replays of a captured graph.  It must not be
  *     shared by calls that may run concurrently.
  *   - A split row's workgroups wait for one another on the device, and every
- *     such wait is bounded.  A wait runs out only when other work keeps the
+ *     such wait is bounded.  The launch plan counts on the device's compute
+ *     units: other work only delays the waits, but two split calls that run
+ *     at the same time on one device (on different streams, or graphs
+ *     replayed concurrently) can each hold compute units that the other's
+ *     workgroups need, so such calls must be ordered (one stream, or events).
+ *     A wait runs out when that is not done, when other work keeps the
  *     device's compute units for a very long time, or when the workspace was
  *     not zero (a stale ticket); the call has already returned ETS_OK by then,
  *     so the kernel records the failure in the workspace's error word (the
