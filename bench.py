@@ -230,14 +230,16 @@ def main() -> int:
                     help="skip the empty-launch and read-only floors")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload lines (C1 .. C5) after the headline")
-    ap.add_argument("--sweep", choices=["batch", "k", "spread"],
+    ap.add_argument("--sweep", choices=["batch", "k", "spread", "split"],
                     help="instead of the headline: one JSON line per point of a sweep, "
                          "'batch' = paged decode rows of 32768 scores, k = 1024, B in "
                          "1 .. 512 (HIP graph and eager launches); 'k' = the C3 workload with "
                          "k in 1 .. 2048; 'spread' = raw rows of up to 262144 scores, "
                          "k = 2048, B in 4 .. 64, lengths all L or uniform in [L/2, L] or "
                          "[L/8, L], the split heuristic's choice against forced "
-                         "workgroups per row (ETS_ROW_SPLIT)")
+                         "workgroups per row (ETS_ROW_SPLIT); 'split' = raw rows of one "
+                         "length, k = 2048, B in 1 .. 512, L in 65536 .. 262144, the "
+                         "heuristic's choice against forced workgroups per row")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a HIP graph")
     ap.add_argument("--host-overhead", action="store_true",
@@ -392,6 +394,50 @@ def sweep_spread(torch, ets, workloads, args, dev, limits, steps) -> int:
     return 0
 
 
+def sweep_split(torch, ets, workloads, args, dev, limits, steps) -> int:
+    """The (B, L) grid behind the split heuristic: raw N(0,1) rows all of
+    length L, k = 2048, timed with the heuristic's choice and with each forced
+    number of workgroups per row that the device allows (ETS_ROW_SPLIT)."""
+    from workloads import Workload
+    k = 2048
+    points = [(B, L) for L in (65536, 131072, 262144)
+              for B in (1, 4, 16, 24, 32, 48, 64, 96, 128, 192, 256, 384, 512)]
+    cap = ets.group_cap(*limits)
+    # the heuristic's own point last: the first launches after a new shape
+    # (new ring buffers) can run slow
+    forced = [0] + [g for g in (2, 3, 4, 5, 6, 8, 10, 12, 16, 32) if g <= cap] + [None]
+    old = os.environ.get("ETS_ROW_SPLIT")
+    try:
+        for B, L in points:
+            rng = np.random.Generator(np.random.PCG64(args.seed + 7 * B + L))
+            x = workloads.normal_dense(rng, B, L)
+            for g in forced:
+                if g is None:
+                    os.environ.pop("ETS_ROW_SPLIT", None)
+                else:
+                    os.environ["ETS_ROW_SPLIT"] = str(g)
+                w = Workload("split-B%d-L%d" % (B, L), "raw", k, B, x, L=L,
+                             lens=np.full(B, L, dtype=np.int32), note="raw, N(0,1), all rows L")
+                rig = Rig(torch, ets, w, dev, limits)
+                us_g = timed(torch, rig.step, steps, args.warmup, False) * 1e3 / steps
+                if rig.ws is not None:
+                    assert ets.workspace_error(rig.ws) == 0, "a bounded wait expired"
+                ab = algorithmic_bytes(w)
+                print(json.dumps({"point": w.name, "B": B, "L": L, "k": k,
+                                  "split": "heuristic" if g is None else "forced",
+                                  "groups": rig.split, "us_per_call_graph": us_g,
+                                  "gb_per_s": ab / (us_g * 1e-6) / 1e9, "calls": steps}),
+                      flush=True)
+                del rig
+                torch.cuda.empty_cache()
+    finally:
+        if old is None:
+            os.environ.pop("ETS_ROW_SPLIT", None)
+        else:
+            os.environ["ETS_ROW_SPLIT"] = old
+    return 0
+
+
 def sweep(torch, ets, workloads, args) -> int:
     """Latency against batch size (the decode caller's flat region), against
     k, or against the spread of row lengths under the split heuristic."""
@@ -402,6 +448,8 @@ def sweep(torch, ets, workloads, args) -> int:
     steps = max(args.steps, 200)
     if args.sweep == "spread":
         return sweep_spread(torch, ets, workloads, args, dev, limits, steps)
+    if args.sweep == "split":
+        return sweep_split(torch, ets, workloads, args, dev, limits, steps)
     points = []
     if args.sweep == "batch":
         L, k, ps = 32768, 1024, 64

@@ -2209,23 +2209,25 @@ int group_kernel_occupancy() {
 // ETS_ROW_SPLIT override above max_group, which the calls reject).  A row
 // that fits one resident 32768-score tile stays on one workgroup: measured on
 // MI355X, the group's exchanges cost more than the work they spread.  Longer
-// rows are cut into chunks of about kGroupChunk scores, at most max_group per
-// row, and the whole grid is held to two workgroups per compute unit unless
-// that would leave a member's chunk larger than one resident tile: a sweep of
-// B in 1..256, row lengths 65536..262144 and 2..64 workgroups per row put the
-// best chunk at 16384 scores while B * G <= 2 * CUs, chunks streamed past one
-// tile well behind resident ones (B = 128, L = 262144: 158 us at G = 4, 99 us
-// at G = 8), and one workgroup per row ahead once B reaches the CU count (the
-// rows alone then keep every compute unit busy) and where more than half the
-// compute units hold a row of at most two tiles (B = 192, L = 65536: 45.7 us
-// one per row, 48.7 at G = 2).  The device is given by its compute units,
-// XCDs and the row-group workgroups one compute unit holds: G is at most one
-// XCD's slots (group_cap_of), and a grid beyond the device's slots keeps G
-// within one shader engine's slots (ticket_cap_of) where chunks of that many
-// members still fit one tile.  cu_count <= 0 (unknown) lifts the grid
-// bounds; an unknown XCD count or occupancy (<= 0) leaves the workspace's
-// slot count as the only cap.  ETS_ROW_SPLIT overrides: 0 or 1 = one
-// workgroup per row, n >= 2 = n workgroups per row, n at most the cap.
+// rows are always split, and the choice is between two member counts: g16,
+// chunks of at most kGroupChunk (16384) scores, and g32, the fewest members
+// whose chunks still fit one resident tile.  A sweep on MI355X (raw rows,
+// k = 2048, B from 1 to 512, L = 65536, 131072 and 262144, G from 2 to 32)
+// placed the best G at:
+//  * the largest G <= g16 whose index grid fits the device at once (one XCD
+//    per row, no member waiting for a workgroup that has not started), as
+//    long as that keeps chunks resident (G >= g32): B = 48, L = 131072 took
+//    17.6 us at G = 5 against 27.9 at G = 8 on a ticketed grid;
+//  * otherwise g32, on a ticketed grid or several index grids, also once the
+//    rows alone fill the compute units: B = 256, L = 262144 took 122 us at
+//    G = 8 against 182 us with one workgroup per row streaming its tiles, and
+//    B = 192, L = 65536 33.5 us at G = 2 against 45.9.
+// The device is given by its compute units, XCDs and the row-group
+// workgroups one compute unit holds: G is at most one XCD's slots
+// (group_cap_of); rows longer than that many tiles stream their chunks.
+// Unknown device facts (<= 0) leave g16 within the workspace's slot count.
+// ETS_ROW_SPLIT overrides: 0 or 1 = one workgroup per row, n >= 2 = n
+// workgroups per row, n at most the cap.
 // Fewest scores per member chunk of a split row: ets::kMinChunk, or the
 // environment variable ETS_MIN_CHUNK (read at every call) when it is an
 // integer >= 1, rounded up to a multiple of 4 and capped at one 32768-score
@@ -2255,28 +2257,15 @@ int32_t split_plan(int32_t B, int64_t max_len, int32_t cu_count, int32_t xcd_cou
     }
   }
   if (max_len <= kRowTile) return 0;
-  int64_t G = std::min((max_len + kGroupChunk - 1) / kGroupChunk, cap);
-  if (cu_count > 0) {
-    if (B >= cu_count) return 0;  // the rows alone keep every compute unit busy
-    if (max_len <= 2 * kRowTile && 2 * static_cast<int64_t>(B) > cu_count) return 0;
-    const int64_t fit = 2 * static_cast<int64_t>(cu_count) / B;  // workgroups per row in 2 * CUs
-    const int64_t resident = (max_len + kRowTile - 1) / kRowTile;  // fewest members whose chunks fit one tile
-    G = std::min(G, std::max(fit, resident));
-  }
-  if (known) {
-    // A grid beyond the device's slots takes tickets only up to one shader
-    // engine's slots; above that it runs as several index grids (see
-    // launch_group).  Measured on MI355X, raw rows, k = 2048: the index grids
-    // cost more than a ticketed grid whose chunks still fit one tile (B = 20
-    // and 32, L = 262144: 28.5 and 31.0 us at G = 16 against 16.9 and 19.4 at
-    // G = 8), but less than a ticketed grid of streamed chunks (B = 16,
-    // L = 600000: 38.3 us at G = 32 against 78.3 at G = 8).
-    const int64_t slots = static_cast<int64_t>(cu_count) * per_cu;
-    const int64_t padded = static_cast<int64_t>(xcd_count) * G * ((B + xcd_count - 1) / xcd_count);
-    const int64_t tcap = ticket_cap_of(cu_count, xcd_count, per_cu);
-    const int64_t resident = (max_len + kRowTile - 1) / kRowTile;
-    if (padded > slots && G > tcap && resident <= tcap) G = tcap;
-  }
+  const int64_t g16 = std::min((max_len + kGroupChunk - 1) / kGroupChunk, cap);
+  const int64_t g32 = std::min((max_len + kRowTile - 1) / kRowTile, cap);
+  if (!known) return static_cast<int32_t>(g16);
+  // the largest G whose index grid (padded to whole rows per XCD) fits the
+  // device's row-group slots at once
+  const int64_t slots = static_cast<int64_t>(cu_count) * per_cu;
+  const int64_t rows_per_xcd = (static_cast<int64_t>(B) + xcd_count - 1) / xcd_count;
+  const int64_t g_index = std::min(g16, slots / (static_cast<int64_t>(xcd_count) * rows_per_xcd));
+  const int64_t G = g_index >= g32 ? g_index : g32;
   return G >= 2 ? static_cast<int32_t>(G) : 0;
 }
 

@@ -246,14 +246,14 @@ int32_t ets_ticket_cap(int32_t cu_count, int32_t xcd_count, int32_t groups_per_c
  * `groups_per_cu` row-group workgroups (ets_device_limits); 0 means one
  * workgroup per row.  Pure host function.
  * Rows that fit one workgroup's 32768-score tile stay whole; longer rows are
- * cut into chunks of about 16384 scores, at most max_group per row, with
- * B * G held to 2 * cu_count as long as every chunk still fits one
- * 32768-score tile; from B >= cu_count on, and for rows of at most 65536
- * scores once B > cu_count / 2, rows stay whole.  G is at most
- * ets_group_cap; a batch whose grid exceeds the device's slots keeps G at
- * most ets_ticket_cap where chunks of that many members still fit one tile
- * (cu_count <= 0 lifts the grid bounds; xcd_count or groups_per_cu <= 0 caps
- * G at 64, the workspace's member slots).
+ * always split, into chunks of about 16384 scores (g16 = ceil(max_row_len /
+ * 16384) members) where one index grid over the batch, xcd_count * G *
+ * ceil(B / xcd_count) workgroups, fits the device's slots (cu_count *
+ * groups_per_cu) at once; otherwise into the largest G below g16 whose index
+ * grid still fits, if its chunks fit one tile; otherwise into the fewest
+ * members whose chunks fit one tile (ceil(max_row_len / 32768)).  G is at
+ * most ets_group_cap (cu_count, xcd_count or groups_per_cu <= 0: g16, at
+ * most 64, the workspace's member slots).
  * The environment variable ETS_ROW_SPLIT, when set to an integer >= 0,
  * overrides the heuristic (0 or 1: one workgroup per row; n: n workgroups per
  * row).  An override above ets_group_cap returns -1, and the selection calls,

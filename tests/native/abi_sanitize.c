@@ -86,9 +86,10 @@ int main(void) {
   unsetenv("ETS_ROW_SPLIT");
   EXPECT(ets_row_split(4, 262144, 256, 8, 1), 16);
   EXPECT(ets_row_split(64, 32768, 256, 8, 1), 0);
-  EXPECT(ets_row_split(192, 65536, 256, 8, 1), 0);
+  EXPECT(ets_row_split(192, 65536, 256, 8, 1), 2);
   EXPECT(ets_row_split(1, (int64_t)1 << 40, 256, 0, 1), 64);
-  EXPECT(ets_row_split(2147483647, (int64_t)1 << 40, 256, 8, 1), 0);
+  EXPECT(ets_row_split(2147483647, (int64_t)1 << 40, 256, 8, 1), 32);
+  EXPECT(ets_row_split(2147483647, 262144, 256, 8, 1), 8);
   setenv("ETS_ROW_SPLIT", "7", 1);
   EXPECT(ets_row_split(4, 262144, 256, 8, 1), 7);
   setenv("ETS_ROW_SPLIT", "33", 1);

@@ -177,46 +177,49 @@ def test_row_split_heuristic():
         # rows that fit one 32768-score workgroup tile stay whole, whatever the batch
         for B, L in ((64, 32768), (128, 32768), (48, 8192), (1, 2048), (4, 4096), (1024, 8192)):
             assert ets.row_split(B, L, 256, 8, 1) == 0, (B, L)
-        # longer rows are cut into chunks of about 16384 scores, at most 32
+        assert ets.row_split(0, 262144, 256, 8, 1) == 0
+        # longer rows: chunks of about 16384 scores while one index grid (8 XCDs
+        # x G x rows per XCD, at most 256 at one workgroup per CU) holds them
         assert ets.row_split(4, 32769, 256, 8, 1) == 3
         assert ets.row_split(4, 65536, 256, 8, 1) == 4
         assert ets.row_split(2, 100000, 256, 8, 1) == 7
+        assert ets.row_split(1, 262144, 256, 8, 1) == 16
         assert ets.row_split(4, 262144, 256, 8, 1) == 16
-        assert ets.row_split(16, 262144, 256, 8, 1) == 16
-        assert ets.row_split(1, 10 ** 7, 256, 8, 1) == 32
-        assert ets.row_split(0, 262144, 256, 8, 1) == 0
-        # the grid is held to two workgroups per compute unit ...
+        assert ets.row_split(16, 262144, 256, 8, 1) == 16  # 8 x 16 x 2 = 256
+        assert ets.row_split(64, 65536, 256, 8, 1) == 4    # 8 x 4 x 8 = 256
+        assert ets.row_split(4, 229000, 256, 8, 1) == 14
+        assert ets.row_split(1, 10 ** 7, 256, 8, 1) == 32  # one XCD's slots
+        # fewer members where that keeps the index grid within the device and
+        # the chunks within one tile
+        assert ets.row_split(20, 262144, 256, 8, 1) == 10  # 8 x 10 x 3 = 240
+        assert ets.row_split(48, 131072, 256, 8, 1) == 5   # 8 x 5 x 6 = 240
+        assert ets.row_split(64, 131072, 256, 8, 1) == 4   # 8 x 4 x 8 = 256
+        assert ets.row_split(128, 65536, 256, 8, 1) == 2   # 8 x 2 x 16 = 256
+        assert ets.row_split(40, 100000, 256, 8, 1) == 6
+        # otherwise the fewest members whose chunks fit one tile, whatever the
+        # batch: a ticketed grid, or several index grids above 8 members
+        assert ets.row_split(32, 262144, 256, 8, 1) == 8
         assert ets.row_split(64, 262144, 256, 8, 1) == 8
-        assert ets.row_split(64, 65536, 256, 8, 1) == 4
-        assert ets.row_split(128, 131072, 256, 8, 1) == 4
-        # ... unless that leaves chunks longer than one 32768-score tile ...
         assert ets.row_split(128, 262144, 256, 8, 1) == 8
+        assert ets.row_split(96, 65536, 256, 8, 1) == 2
+        assert ets.row_split(192, 65536, 256, 8, 1) == 2
         assert ets.row_split(192, 131072, 256, 8, 1) == 4
-        # ... but rows of at most two tiles stay whole once B > CUs / 2
-        assert ets.row_split(192, 65536, 256, 8, 1) == 0
-        assert ets.row_split(128, 65536, 256, 8, 1) == 4
+        assert ets.row_split(256, 65536, 256, 8, 1) == 2
+        assert ets.row_split(256, 262144, 256, 8, 1) == 8
+        assert ets.row_split(4096, 262144, 256, 8, 1) == 8
+        assert ets.row_split(16, 600000, 256, 8, 1) == 19
+        # rows longer than 32 tiles: one XCD's slots, chunks streamed
         assert ets.row_split(64, 10 ** 7, 256, 8, 1) == 32
-        # ... and rows stay whole once the batch alone fills the device
-        assert ets.row_split(256, 65536, 256, 8, 1) == 0
-        assert ets.row_split(4096, 262144, 256, 8, 1) == 0
-        # an unknown compute-unit count lifts the bound
+        # two row-group workgroups per CU: 512 slots
+        assert ets.row_split(20, 262144, 256, 8, 2) == 16  # 8 x 16 x 3 = 384
+        # the device's group cap bounds G (one XCD's slots: 20 for 160 CUs in 8 XCDs)
+        assert ets.row_split(1, 10 ** 7, 160, 8, 1) == 20
+        # unknown device facts: chunks of about 16384, within the 64 record slots
         assert ets.row_split(4, 262144, 0, 8, 1) == 16
         assert ets.row_split(4096, 262144, 0, 8, 1) == 16
-        # the device's group cap bounds G (one XCD's slots: 20 for 160 CUs in 8
-        # XCDs); an unknown XCD count or occupancy leaves the 64 record slots
-        assert ets.row_split(1, 10 ** 7, 160, 8, 1) == 20
         assert ets.row_split(1, 10 ** 7, 256, 0, 1) == 64
         assert ets.row_split(1, 10 ** 7, 256, 8, 0) == 64
         assert ets.row_split(1, 10 ** 7, 256, 8, 4) == 64
-        # a grid beyond the device's slots keeps G within one shader engine's
-        # slots (8) where chunks of 8 members still fit one tile ...
-        assert ets.row_split(20, 262144, 256, 8, 1) == 8
-        assert ets.row_split(32, 262144, 256, 8, 1) == 8
-        assert ets.row_split(48, 200000, 256, 8, 1) == 8
-        assert ets.row_split(16, 262144, 256, 8, 1) == 16  # 256 workgroups: fits
-        assert ets.row_split(20, 262144, 256, 8, 2) == 16  # two per CU: 384 of 512 slots
-        # ... and keeps the heuristic's G where they would not (several index grids)
-        assert ets.row_split(16, 600000, 256, 8, 1) == 32
     finally:
         if env is not None:
             os.environ["ETS_ROW_SPLIT"] = env
@@ -224,28 +227,26 @@ def test_row_split_heuristic():
 
 def test_row_split_bounds_hold_everywhere():
     """Over a grid of shapes and devices: at most one XCD's row-group slots per
-    row, never a split of a row that fits one 32768-score tile or of a batch
-    that fills the device, the grid within two workgroups per compute unit
-    unless chunks would outgrow one tile, and a grid beyond the device's slots
-    above one shader engine's slots only where chunks that many members would
-    give outgrow one tile."""
+    row; a row that fits one 32768-score tile is never split and a longer one
+    always is; chunks of at most 16384 scores are never cut further; chunks
+    stay within one tile where the cap allows; and a G above the fewest
+    members with resident chunks only where its index grid fits the device."""
     import exact_top_selection_amd as ets
     env = os.environ.pop("ETS_ROW_SPLIT", None)
     try:
         for cu, nx in ((80, 1), (256, 8), (304, 8)):
-            cap, tcap = ets.group_cap(cu, nx, 1), ets.ticket_cap(cu, nx, 1)
+            cap = ets.group_cap(cu, nx, 1)
             for B in (1, 2, 3, 5, 8, 17, 64, 100, 128, 129, 256, 1000):
                 for L in (1, 32768, 32769, 65536, 100000, 262144, 10 ** 6, 2 ** 31 - 1):
                     g = ets.row_split(B, L, cu, nx, 1)
                     assert 0 <= g <= cap, (cu, B, L, g)
-                    if L <= 32768 or B >= cu:
-                        assert g == 0, (cu, B, L, g)
+                    assert (g == 0) == (L <= 32768), (cu, B, L, g)
                     if g:
                         tiles = -(-L // 32768)
-                        assert g >= 2 and B * g <= max(2 * cu, B * tiles), (cu, B, L, g)
-                        padded = nx * g * -(-B // nx)
-                        if padded > cu and g > tcap:
-                            assert tiles > tcap, (cu, B, L, g)
+                        g16 = min(-(-L // 16384), cap)
+                        assert min(tiles, cap) <= g <= g16, (cu, B, L, g)
+                        if g > min(tiles, cap):
+                            assert nx * g * -(-B // nx) <= cu, (cu, B, L, g)
     finally:
         if env is not None:
             os.environ["ETS_ROW_SPLIT"] = env

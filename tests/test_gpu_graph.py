@@ -75,17 +75,19 @@ def test_graph_replays_match_the_oracle():
 def test_graph_replays_of_batches_beyond_the_device():
     """Inside one captured graph: a batch whose grid exceeds the device with G
     above one shader engine's slots (B = 40, G = 16: three index grids of 16,
-    16 and 8 rows) and a ticketed batch (B = 64, L = 131072: the default G =
-    8).  Every replay matches the oracle, with the error word zero and both
-    workspaces clean."""
+    16 and 8 rows) and a ticketed batch (B = 96, L = 131072: the default G =
+    4, a grid of 384 workgroups).  Every replay matches the oracle, with the
+    error word zero and both workspaces clean."""
     import os
     from workloads import Workload
     d = torch.device("cuda:0")
     rng = np.random.Generator(np.random.PCG64(60))
     w1 = Workload("graph-grids", "raw", 1024, 40, workloads.normal_dense(rng, 40, 100000), L=100000)
-    w2 = Workload("graph-ticket", "raw", 2048, 64, workloads.normal_dense(rng, 64, 131072), L=131072)
+    w2 = Workload("graph-ticket", "raw", 2048, 96, workloads.normal_dense(rng, 96, 131072), L=131072)
     cu, nx, occ = ets.device_limits()
-    assert ets.row_split(w2.B, w2.L, cu, nx, occ) == ets.ticket_cap(cu, nx, occ)
+    g2 = ets.row_split(w2.B, w2.L, cu, nx, occ)
+    # a ticketed grid: beyond the device's slots, G within one engine's
+    assert 2 <= g2 <= ets.ticket_cap(cu, nx, occ) and nx * g2 * -(-w2.B // nx) > cu * occ
     s1, s2 = torch.from_numpy(w1.scores).to(d), torch.from_numpy(w2.scores).to(d)
     want1, want2 = run_oracle(w1), run_oracle(w2)
     g1 = torch.full((w1.B, w1.k), -7, dtype=torch.int32, device=d)

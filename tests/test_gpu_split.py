@@ -488,11 +488,13 @@ def test_split_override_above_cap_is_rejected():
         assert out.shape == (2, 64)
 
 
-@pytest.mark.parametrize("B,L,k", [(128, 262144, 2048), (192, 131072, 1024), (192, 65536, 1024)])
+@pytest.mark.parametrize("B,L,k", [(128, 262144, 2048), (192, 131072, 1024), (192, 65536, 1024),
+                                   (256, 262144, 2048)])
 def test_default_heuristic_large_batches(B, L, k):
     """The heuristic's choices for long rows at large batches: chunks of 32768
-    scores held in registers on a ticketed grid (B = 128, L = 262144: G = 8;
-    B = 192, L = 131072: G = 4) and whole streamed rows (B = 192, L = 65536)."""
+    scores held in registers on a ticketed grid (B = 128 and 256, L = 262144:
+    G = 8; B = 192, L = 131072: G = 4; B = 192, L = 65536: G = 2), also where
+    the rows alone would fill the compute units."""
     limits = ets.device_limits()
     print("case default B", B, "L", L, "G", ets.row_split(B, L, *limits), flush=True)
     rng = np.random.Generator(np.random.PCG64(B * 7 + L))
@@ -570,9 +572,10 @@ def test_stale_ticket_sets_the_error_word():
     the same workspace is exact again."""
     d = dev()
     limits = ets.device_limits()
-    B, L, k = 64, 131072, 2048
+    cu, nx, occ = limits
+    B, L, k = 96, 131072, 2048
     G = ets.row_split(B, L, *limits)
-    assert G * B > limits[0], "needs a ticketed grid"
+    assert 2 <= G <= ets.ticket_cap(*limits) and nx * G * -(-B // nx) > cu * occ, "needs a ticketed grid"
     x = workloads.normal_dense(np.random.Generator(np.random.PCG64(3)), B, L)
     s = torch.from_numpy(x).to(d)
     ws = ets.new_workspace(B, L, k, d)
