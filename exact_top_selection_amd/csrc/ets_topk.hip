@@ -1886,6 +1886,22 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   }
   if (tid < kSmallCap) sm.cand[tid] = 0ull;
   __syncthreads();
+  // ---- return the row's workspace to zero before the tie list is resolved,
+  // so that the stores land meanwhile: every member has arrived, after its
+  // last read of the slots, the tables and the record, and every wave here
+  // has read the cursor (barrier above).  The last round's table (round 0:
+  // its coarse bins; earlier rounds were cleared on the way) and the record.
+  {
+    const int lastr = round - 1;
+    clear_bins<T>(ghist + (lastr % 3) * kHistBins, lastr == 0 ? kCoarseBins : kHistBins);
+    if (tid < G) st_dev(slots + tid, 0ull);
+    if (tid == 0) {
+      st_dev(rec + kRecBarrier, 0u);
+      st_dev(rec + kRecDone, 0u);
+      st_dev(rec + kRecBelow, 0u);
+      st_dev(reinterpret_cast<uint64_t*>(rec + kRecCursor), 0ull);
+    }
+  }
   const int trips = static_cast<int>((m + T - 1) / T);
   const uint32_t tpad = static_cast<uint32_t>(trips) * T - m;
   // every lane visits the same number of slots (the radix rounds vote per wave);
@@ -1916,19 +1932,6 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   rank_bucket<T>(sm.cand, min(sm.ccount, static_cast<uint32_t>(kSmallCap)), fin.kk, first2,
                  [&](uint32_t slot, int32_t pos) { r.out[slot] = map_any(pos); });
 
-  // ---- return the row's workspace to zero: the last round's table (round 0:
-  // its coarse bins; earlier rounds were cleared on the way) and the record
-  const int lastr = round - 1;
-  clear_bins<T>(ghist + (lastr % 3) * kHistBins, lastr == 0 ? kCoarseBins : kHistBins);
-  // every member has read the slots: it has arrived after its exchange
-  if (tid < G) st_dev(slots + tid, 0ull);
-  __syncthreads();  // every wave has read the record before it is reset
-  if (tid == 0) {
-    st_dev(rec + kRecBarrier, 0u);
-    st_dev(rec + kRecDone, 0u);
-    st_dev(rec + kRecBelow, 0u);
-    st_dev(reinterpret_cast<uint64_t*>(rec + kRecCursor), 0ull);
-  }
 }
 
 // G workgroups per row.  TICKET: B * G workgroups take rows in the order
