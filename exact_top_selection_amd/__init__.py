@@ -34,7 +34,8 @@ __all__ = ["topk_raw", "topk_paged", "topk_ragged", "topk_paged_noalloc", "works
 MAX_K = 2048
 NOALLOC_SCRATCH_BYTES = 4 << 20  # ETS_NOALLOC_SCRATCH_BYTES: topk_paged_noalloc's static scratch
 # bits of a workspace's error word (workspace_error): which wait ran out
-ERROR_BITS = {1: "bounds exchange", 2: "stale ticket", 4: "coarse histogram", 8: "round barrier"}
+ERROR_BITS = {1: "bounds exchange", 2: "stale ticket", 4: "coarse histogram", 8: "round barrier",
+              16: "tie list"}
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libets_topk.so")
 _lock = threading.Lock()

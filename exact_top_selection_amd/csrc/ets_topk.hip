@@ -1271,12 +1271,13 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // once on one device (on different streams) can each hold slots that the
 // other's missing members need.  Every wait is bounded; on expiry the
 // workspace's error word gets the bit of that wait (bounds exchange, coarse
-// table or round barrier), the call's output is undefined, and the kernel
-// still ends.
+// table, round barrier or tie list), the call's output is undefined, and the
+// kernel still ends.
 
 // Data crosses workgroups only through agent-scope relaxed atomics, with each
-// wave's memory counter drained before an arrival is counted (or, for the
-// coarse table, completion read from the table's own total).  Why this is
+// wave's memory counter drained before a round barrier's arrival is counted
+// (or, for the coarse table and the tie list, completion read from the data
+// itself).  Why this is
 // enough on gfx942/gfx950 (LLVM AMDGPU usage guide, "Memory Model GFX942",
 // which gfx950 follows): an agent-scope atomic load, store or
 // read-modify-write is issued with the sc1 bit, so it is performed at the
@@ -1289,13 +1290,15 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 // workgroup writes and another reads (slots, tables, counters, cursor, tie
 // list) is written and read by such atomics, so no ordinary access needs the
 // write-back or the invalidate, and the completion wait is drain_vmem()
-// before the arrival that publishes the data.  The output rows are written
+// before the arrival that publishes the data.  Two hand-offs need no such
+// wait, because the reader sees completion in the data itself: the coarse
+// table, whose total reaches n only once every add has landed, and the tie
+// list, whose entries are never 0 once written.  The output rows are written
 // with ordinary stores but never read inside the kernel.
 //
 // Workspace (u32 words): hdr[64], then per row rec[192] (counters, then one
 // u64 slot per member) | hist[3][4096] | ties[kTieCap] (u64).  It must be
-// zero before its first use; every call returns the header, the records and
-// the tables to zero (tie lists may keep stale entries).
+// zero before its first use; every call returns all of it to zero.
 
 constexpr int kTieCap = 4096;      // tie-list entries per row
 // Scores per member of a split row: n / G rounded up to a multiple of 4
@@ -1329,7 +1332,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 
 enum HdrField : int { kHdrTicket = 0, kHdrFinished = 16, kHdrError = 32 };
 // Bits of the error word: which bounded wait ran out, or a stale ticket.
-enum ErrBit : uint32_t { kErrBounds = 1u, kErrStale = 2u, kErrCoarse = 4u, kErrBarrier = 8u };
+enum ErrBit : uint32_t { kErrBounds = 1u, kErrStale = 2u, kErrCoarse = 4u, kErrBarrier = 8u, kErrTies = 16u };
 enum GroupRecField : int { kRecBarrier = 0, kRecDone = 16, kRecCursor = 32 /* u64 */,
                           kRecBelow = 48, kRecSlots = 64 /* u64 per member */ };
 
@@ -1354,6 +1357,13 @@ __device__ __forceinline__ void or_dev(uint32_t* p, uint32_t v) {
 }
 // Waits until every global access this wave issued has completed.
 __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A tie-list entry: the key in the high word, the complement of the position
+// (never 0, as positions are below 2^31) in the low word, so that an entry
+// still in flight reads as 0 in a list that every call returns to zero.
+__device__ __forceinline__ uint64_t tie_word(uint32_t key, uint32_t pos) {
+  return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~pos);
+}
 
 // Arrives at a row's barrier and returns once `target` arrivals are counted.
 // Every thread calls it; what each thread wrote before has completed by the
@@ -1836,14 +1846,14 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
       cmask &= cmask - 1u;
       const uint32_t pos = static_cast<uint32_t>(span.start + tile_pos<T, V4>(j));
       if (ob < static_cast<uint32_t>(kTieCap))
-        st_dev(gties + ob, (static_cast<uint64_t>(select_slot<PT>(key, j)) << 32) | pos);
+        st_dev(gties + ob, tie_word(select_slot<PT>(key, j), pos));
       ++ob;
     }
   } else {
     for_each([&](uint32_t x, int32_t pos, int) {
       if (sel_bucket(sel, nm1, cend, x, pos)) {
         if (ob < static_cast<uint32_t>(kTieCap))
-          st_dev(gties + ob, (static_cast<uint64_t>(x) << 32) | static_cast<uint32_t>(pos));
+          st_dev(gties + ob, tie_word(x, static_cast<uint32_t>(pos)));
         ++ob;
       }
     });
@@ -1868,17 +1878,32 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     }
   }
 
-  // ---- the group's last workgroup resolves the tie list
-  drain_vmem();
+  // ---- the group's last workgroup resolves the tie list.  No wave waits for
+  // its stores before the arrival: the output is not read here, and the last
+  // workgroup waits for each tie-list entry itself.
   __syncthreads();
   if (tid == 0) sm.last = (add_dev(rec + kRecDone, 1u) == static_cast<uint32_t>(G - 1)) ? 1u : 0u;
   __syncthreads();
   if (!sm.last) return;
   const uint32_t m = min(static_cast<uint32_t>(ld_dev(reinterpret_cast<const uint64_t*>(rec + kRecCursor))),
                          static_cast<uint32_t>(kTieCap));
+  // every entry below m was stored by a member that has arrived; one still in
+  // flight reads as 0.  A wait past kSpinLimit polls sets kErrTies and takes
+  // the entry as padding (key 0 at position n), which selects nothing.
   for (uint32_t i = tid; i < m; i += T) {
-    const uint64_t v = ld_dev(gties + i);
-    sm.u.ties[i] = make_uint2(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(v));
+    uint64_t v = ld_dev(gties + i);
+    uint32_t spins = 0;
+    while (static_cast<uint32_t>(v) == 0u && spins <= kSpinLimit) {
+      __builtin_amdgcn_s_sleep(1);
+      v = ld_dev(gties + i);
+      ++spins;
+    }
+    if (static_cast<uint32_t>(v) == 0u) {
+      or_dev(err, kErrTies);
+      sm.u.ties[i] = make_uint2(0u, static_cast<uint32_t>(n));
+    } else {
+      sm.u.ties[i] = make_uint2(static_cast<uint32_t>(v >> 32), ~static_cast<uint32_t>(v));
+    }
   }
   if (tid == 0) {
     sm.wcount = 0;
@@ -1894,6 +1919,7 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   {
     const int lastr = round - 1;
     clear_bins<T>(ghist + (lastr % 3) * kHistBins, lastr == 0 ? kCoarseBins : kHistBins);
+    for (uint32_t i = tid; i < m; i += T) st_dev(gties + i, 0ull);  // entries this thread read
     if (tid < G) st_dev(slots + tid, 0ull);
     if (tid == 0) {
       st_dev(rec + kRecBarrier, 0u);

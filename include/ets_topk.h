@@ -42,9 +42,9 @@
  *     counters through it (sglang PR #37591 digest, the topk.hip excerpt:
  *     the caller's allocator provides the row-split workspace).  It must be
  *     zero-filled before its first use (ets_workspace_init, or any zero fill)
- *     and every call returns the counters and tables it relies on to zero
- *     (other words may keep stale data), so one workspace serves any number
- *     of calls, including replays of a captured graph.  It must not be
+ *     and every call returns it to zero (counters, tables and tie lists), so
+ *     one workspace serves any number of calls, including replays of a
+ *     captured graph.  It must not be
  *     shared by calls that may run concurrently.
  *   - A split row's workgroups wait for one another on the device, and every
  *     such wait is bounded.  The launch plan counts on the device's compute
@@ -206,7 +206,7 @@ ets_status ets_workspace_init(void* workspace, size_t bytes, void* stream);
  * is an OR of bits: 2 marks a stale ticket (a workspace that was not zero);
  * the others name the bounded wait that ran out: 1 the exchange of the row's
  * bounds, 4 the poll of the row's coarse histogram, 8 a barrier between
- * radix rounds.
+ * radix rounds, 16 the wait for the row's tie-list entries.
  * workspace_bytes = 0 (a call that needed no workspace) writes 0; otherwise
  * workspace must be 16-byte aligned and at least 256 bytes.  Nothing is
  * synchronised: read flag after the stream reaches it.

@@ -21,11 +21,11 @@ def dev():
 # 4096-bin tables and a 4096-entry u64 tie list.
 WS_HDR = 64
 WS_ROW = 192 + 3 * 4096 + 2 * 4096
-WS_KEPT_ZERO = 192 + 3 * 4096  # record, member slots, tables: back at zero after every call
+WS_KEPT_ZERO = WS_ROW  # record, member slots, tables and tie list: back at zero after every call
 
 
 def workspace_dirty(ws: torch.Tensor) -> int:
-    """Non-zero words among the header, records and tables of a workspace."""
+    """Non-zero words of a workspace: header, records, tables and tie lists."""
     torch.cuda.synchronize()
     w = ws.view(torch.int32)
     B = (w.numel() - WS_HDR) // WS_ROW

@@ -269,12 +269,12 @@ def test_error_bits_match_the_header_and_the_kernels():
     text = " ".join(open(HEADER).read().replace("\n *", "\n").split())
     assert "2 marks a stale ticket" in text
     for bit, words in ((1, "the exchange of the row's bounds"), (4, "the poll of the row's coarse histogram"),
-                       (8, "a barrier between radix rounds")):
+                       (8, "a barrier between radix rounds"), (16, "the wait for the row's tie-list entries")):
         assert "%d %s" % (bit, words) in text, bit
     src = open(os.path.join(ROOT, "exact_top_selection_amd", "csrc", "ets_topk.hip")).read()
     enum = re.search(r"enum ErrBit : uint32_t \{([^}]*)\}", src).group(1)
     vals = {name.strip(): int(v.strip().rstrip("u"), 0) for name, v in
             (item.split("=") for item in enum.split(","))}
-    assert vals == {"kErrBounds": 1, "kErrStale": 2, "kErrCoarse": 4, "kErrBarrier": 8}
-    assert sorted(ets.ERROR_BITS) == [1, 2, 4, 8]
+    assert vals == {"kErrBounds": 1, "kErrStale": 2, "kErrCoarse": 4, "kErrBarrier": 8, "kErrTies": 16}
+    assert sorted(ets.ERROR_BITS) == [1, 2, 4, 8, 16]
     assert ets.ERROR_BITS[2] == "stale ticket"

@@ -50,13 +50,13 @@ def _raw(name, x, k, lens=None):
 
 
 def _assert_clean(ws):
-    """The error word is zero, and so are the counters and histogram tables a
-    call relies on; the tie lists behind them may keep stale entries."""
+    """The error word is zero, and so is the rest of the workspace: counters,
+    histogram tables and tie lists."""
     torch.cuda.synchronize()
     e = ets.workspace_error(ws)
     assert e == 0, "a call stopped waiting for its row group (error word %d)" % e
     nz = workspace_dirty(ws)
-    assert nz == 0, "%d counter or table words left non-zero" % nz
+    assert nz == 0, "%d workspace words left non-zero" % nz
 
 
 def _cached_workspaces():
