@@ -1239,10 +1239,12 @@ __global__ __launch_bounds__(T) void row_topk_kernel(Params p) {
 //    narrowed by further rounds of 12-bit digits of the key, then of the
 //    position among equal keys;
 //  * every member writes its winners to the output and appends its bucket
-//    members to the row's tie list, both placed through one 64-bit cursor;
-//  * the last member of the group to finish ranks the tie list exactly
-//    (LDS radix rounds, then direct comparison), emits the rest of the row
-//    and returns the row's workspace to zero.
+//    members to the row's tie list, both placed through one 64-bit cursor
+//    whose top byte also counts the members that have taken it;
+//  * the last member to take the cursor waits for each tie-list entry (an
+//    entry is never 0 once written), ranks the list exactly (LDS radix
+//    rounds, then direct comparison), emits the rest of the row and returns
+//    the row's workspace to zero.
 //
 // Members are assigned by workgroup index, a row's G members on one XCD,
 // when the whole grid fits the device's row-group slots at once; otherwise
@@ -1333,7 +1335,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 enum HdrField : int { kHdrTicket = 0, kHdrFinished = 16, kHdrError = 32 };
 // Bits of the error word: which bounded wait ran out, or a stale ticket.
 enum ErrBit : uint32_t { kErrBounds = 1u, kErrStale = 2u, kErrCoarse = 4u, kErrBarrier = 8u, kErrTies = 16u };
-enum GroupRecField : int { kRecBarrier = 0, kRecDone = 16, kRecCursor = 32 /* u64 */,
+enum GroupRecField : int { kRecBarrier = 0, kRecCursor = 32 /* u64 */,
                           kRecBelow = 48, kRecSlots = 64 /* u64 per member */ };
 
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
@@ -1550,7 +1552,7 @@ struct alignas(16) GroupSmem {
   } u;
   uint32_t wsum2[16];
   uint32_t ticket, last, wcount, ccount;
-  uint32_t base[2];
+  uint32_t base[3];
 };
 
 // One chunk [span.start, span.end) of row b as member g of its row's group.
@@ -1814,10 +1816,15 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   uint32_t ow = iw - nw + sum_other_waves<W, true>(sm.sel.wsum);
   uint32_t ob = ib - nb + sum_other_waves<W, true>(sm.wsum2);
   if (tid == T - 1) {
-    const uint64_t add = (static_cast<uint64_t>(ow + nw) << 32) | (ob + nb);
+    // one atomic places this member's winners (bits 32..55: at most k of a
+    // row) and bucket members (bits 0..31), and counts its arrival (bits
+    // 56..63): the member that takes it last resolves the tie list
+    const uint64_t add = (1ull << 56) | (static_cast<uint64_t>(ow + nw) << 32) | (ob + nb);
     const uint64_t old = add_dev(reinterpret_cast<uint64_t*>(rec + kRecCursor), add);
-    sm.base[0] = static_cast<uint32_t>(old >> 32);
+    sm.base[0] = static_cast<uint32_t>(old >> 32) & 0xFFFFFFu;
     sm.base[1] = static_cast<uint32_t>(old);
+    sm.base[2] = static_cast<uint32_t>(old) + ob + nb;  // the row's bucket total, if last
+    sm.last = static_cast<uint32_t>(old >> 56) == static_cast<uint32_t>(G - 1) ? 1u : 0u;
     sm.wcount = ow + nw;
   }
   // the winners' chunk-local slots need no cursor: placed while it returns
@@ -1878,17 +1885,15 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     }
   }
 
-  // ---- the group's last workgroup resolves the tie list.  No wave waits for
-  // its stores before the arrival: the output is not read here, and the last
-  // workgroup waits for each tie-list entry itself.
-  __syncthreads();
-  if (tid == 0) sm.last = (add_dev(rec + kRecDone, 1u) == static_cast<uint32_t>(G - 1)) ? 1u : 0u;
+  // ---- the group's last workgroup (the last to take the cursor) resolves
+  // the tie list.  No wave waits for its stores: the output is not read
+  // here, and the last workgroup waits for each tie-list entry itself.  The
+  // barrier: every wave is done with this workgroup's winners in LDS.
   __syncthreads();
   if (!sm.last) return;
-  const uint32_t m = min(static_cast<uint32_t>(ld_dev(reinterpret_cast<const uint64_t*>(rec + kRecCursor))),
-                         static_cast<uint32_t>(kTieCap));
-  // every entry below m was stored by a member that has arrived; one still in
-  // flight reads as 0.  A wait past kSpinLimit polls sets kErrTies and takes
+  const uint32_t m = min(sm.base[2], static_cast<uint32_t>(kTieCap));
+  // every entry below m was stored, or is being stored, by a member that has
+  // taken the cursor; one still in flight reads as 0.  A wait past kSpinLimit polls sets kErrTies and takes
   // the entry as padding (key 0 at position n), which selects nothing.
   for (uint32_t i = tid; i < m; i += T) {
     uint64_t v = ld_dev(gties + i);
@@ -1912,10 +1917,11 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   if (tid < kSmallCap) sm.cand[tid] = 0ull;
   __syncthreads();
   // ---- return the row's workspace to zero before the tie list is resolved,
-  // so that the stores land meanwhile: every member has arrived, after its
-  // last read of the slots, the tables and the record, and every wave here
-  // has read the cursor (barrier above).  The last round's table (round 0:
-  // its coarse bins; earlier rounds were cleared on the way) and the record.
+  // so that the stores land meanwhile: every member has taken the cursor,
+  // after its last read of the slots, the tables and the record, and every
+  // tie-list entry has landed (read above).  The last round's table (round
+  // 0: its coarse bins; earlier rounds were cleared on the way) and the
+  // record.
   {
     const int lastr = round - 1;
     clear_bins<T>(ghist + (lastr % 3) * kHistBins, lastr == 0 ? kCoarseBins : kHistBins);
@@ -1923,7 +1929,6 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     if (tid < G) st_dev(slots + tid, 0ull);
     if (tid == 0) {
       st_dev(rec + kRecBarrier, 0u);
-      st_dev(rec + kRecDone, 0u);
       st_dev(rec + kRecBelow, 0u);
       st_dev(reinterpret_cast<uint64_t*>(rec + kRecCursor), 0ull);
     }
