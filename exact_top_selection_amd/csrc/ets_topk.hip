@@ -1893,8 +1893,9 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
   if (!sm.last) return;
   const uint32_t m = min(sm.base[2], static_cast<uint32_t>(kTieCap));
   // every entry below m was stored, or is being stored, by a member that has
-  // taken the cursor; one still in flight reads as 0.  A wait past kSpinLimit polls sets kErrTies and takes
-  // the entry as padding (key 0 at position n), which selects nothing.
+  // taken the cursor; one still in flight reads as 0.  A wait past
+  // kSpinLimit polls sets kErrTies and takes the entry as padding (key 0 at
+  // position n), which selects nothing.
   for (uint32_t i = tid; i < m; i += T) {
     uint64_t v = ld_dev(gties + i);
     uint32_t spins = 0;
