@@ -1819,6 +1819,8 @@ __device__ __forceinline__ void group_row(const Params& p, GroupSmem& sm, const 
     // one atomic places this member's winners (bits 32..55: at most k of a
     // row) and bucket members (bits 0..31), and counts its arrival (bits
     // 56..63): the member that takes it last resolves the tie list
+    static_assert(ETS_MAX_K < (1 << 24), "a row's winners fit 24 bits");
+    static_assert((kRecWords - kRecSlots) / 2 < 256, "a row's member slots fit 8 bits");
     const uint64_t add = (1ull << 56) | (static_cast<uint64_t>(ow + nw) << 32) | (ob + nb);
     const uint64_t old = add_dev(reinterpret_cast<uint64_t*>(rec + kRecCursor), add);
     sm.base[0] = static_cast<uint32_t>(old >> 32) & 0xFFFFFFu;
